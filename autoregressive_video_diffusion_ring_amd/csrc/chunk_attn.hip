@@ -1,0 +1,871 @@
+// Block-causal chunk attention over the ring cache (gfx950, MFMA).
+//
+// Each call attends the chunk's new queries over every cached slot
+// (Runway Characters, abstract), with a scalar bias added to the logits of
+// earlier blocks (video-conductor, "Plastic Windows") and a block-causal mask
+// (StreamLTX project page, Training).
+//
+// Work split.  A workgroup owns 128 queries of one head and runs 8 waves: 4
+// query sub-tiles of 32 x 2 key halves.  Half k walks the tiles k, k+2, ...
+// of 64 slots; at the end the two halves of each query sub-tile merge their
+// softmax states through LDS.  Tiles reach LDS by direct global->LDS loads
+// (no registers) three stages ahead; each half has its own stage buffers.
+//
+// Formulation.  A wave computes S^T = K Q^T with 32x32 MFMAs, so the
+// accumulator gives every lane ONE query (column l % 32) and 32 slots: the
+// online-softmax state (running max, running sum, output row) is per lane and
+// the only cross-lane step is one swap with lane l ^ 32 (the other 32 slots
+// of the same query).  The output stays transposed: O^T = V^T P^T.  The A
+// operand of the first MFMA reads K rows in a permuted order chosen so that
+// lane group g = l / 32 ends up holding slots 32g .. 32g+31 of the tile: the
+// probabilities then sit in exactly the register order the P^T operand of the
+// second MFMA needs, and V^T is read in natural slot order.
+//
+// Scales (FP8 cache).  With per-slot K and V scales and a per-workgroup Q
+// scale, one logit in log2 units is  y0 = c * s_k[slot] * (Qc . Kc) + bias2
+// with c = softmax_scale * log2(e) * s_q.  V's per-slot scale varies along the
+// reduction axis of P V, so it is folded into the exponent:
+//   y  = y0 + log2(s_v[slot]),   P~ = 2^(y - m) = p * s_v,   l += P~ / s_v
+// so O = sum P~ Vc needs no further scaling and P~ <= 2^tau for the running
+// stabiliser m.  Per slot, c*s_k, log2 s_v (+ bias2) and 1/s_v are computed
+// once per tile into LDS; a score then costs one FMA, half a max, a subtract,
+// an exp2, one FMA for the sum and half an FP8 conversion.  The stabiliser is
+// only raised when a tile's maximum exceeds it by more than tau = 8 (log2),
+// which keeps P~ <= 256 inside e4m3's range and makes O rescales rare.
+//
+// Masks.  A tile whose 64 slots are all visible to all of the wave's queries
+// with one bias value takes the fast path; other tiles evaluate visibility
+// and bias per (slot, query) from the slot's block id; tiles no query of the
+// wave can see are skipped.  Slots are walked in physical order: softmax does
+// not depend on slot order, so a wrapped ring needs no special case.
+#include <cmath>
+#include <type_traits>
+
+#include "rc_device.h"
+#include "rc_kernels.h"
+
+namespace rc {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// LDS reads use native vector types: a 16-byte read then reaches the backend
+// as one load that keeps its alias information, which the wait insertion
+// needs to see that it does not depend on loads in flight to other stages.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void glb_void;
+
+constexpr int kKT = 64;       // slots per tile
+constexpr int kQW = 32;       // queries per wave
+constexpr int kQSub = 4;      // query sub-tiles per workgroup
+constexpr int kHalves = 2;    // key halves per workgroup
+constexpr int kWaves = kQSub * kHalves;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kQT = kQW * kQSub;  // queries per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.f;            // lazy-rescale threshold, log2 units
+constexpr float kMinVScale = 0x1p-60f; // floor for log2 / reciprocal of s_v
+
+template <int KV>
+struct KvT {
+  static constexpr int es = KV == KV_F32 ? 4 : (KV == KV_BF16 ? 2 : 1);
+};
+
+struct AttnArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* slot_block;
+  int N, H, v_ld;
+  const void* q;
+  int n_q, q_pos0, q_block0, q_block_len;
+  float bias_log2;   // cache_bias * log2(e)
+  float scale_log2;  // softmax_scale * log2(e)
+  void* out;
+  float* lse;
+  float* part_o;    // [splits][n_q][H][d] when split
+  float* part_lse;  // [splits][H][n_q]
+  int n_qt, n_splits, tiles_per_split, n_tiles;
+  int remap;  // blockIdx -> work item remap keeps a head's tiles on one XCD
+  int use_rope;
+  RopeTable rope;
+};
+
+// LDS geometry of one tile buffer.
+template <int KV, int D>
+struct Tile {
+  static constexpr int es = KvT<KV>::es;
+  static constexpr int k_row = D * es;  // bytes per K row
+  static constexpr int k_cpr = k_row / 16;
+  static constexpr int v_row = kKT * es;  // bytes per V^T row
+  static constexpr int v_cpr = v_row / 16;
+  static constexpr int k_off = 0;
+  static constexpr int v_off = kKT * k_row;
+  static constexpr int raw_off = v_off + D * v_row;  // k_scale[64], v_scale[64], block[64]
+  static constexpr int kfc_off = raw_off + 768;      // c * s_k
+  static constexpr int lv0_off = kfc_off + 256;      // log2 s_v
+  static constexpr int lv1_off = lv0_off + 256;      // log2 s_v + bias2
+  static constexpr int ivf_off = lv1_off + 256;      // 1 / s_v
+  static constexpr int bytes = ivf_off + 256;
+  static constexpr int k_instr = kKT * k_cpr / (kQSub * kWave);  // 16-byte DMA per wave
+  static constexpr int v_instr = D * v_cpr / (kQSub * kWave);
+  static_assert(kKT * k_cpr % (kQSub * kWave) == 0 && D * v_cpr % (kQSub * kWave) == 0, "tile split");
+};
+
+template <int KV, int D>
+struct Stages {
+  // Double buffering; each stage holds kps tiles per key half (two when they
+  // fit), so a tile's loads are issued two tile-computations ahead.
+  static constexpr int rope_bytes = (64 + 8 * 64 + 16 * 64) * 8;
+  static constexpr int avail = 160 * 1024 - rope_bytes - 256;
+  static constexpr int kps = 2 * kHalves * 2 * Tile<KV, D>::bytes <= avail ? 2 : 1;
+  static_assert(2 * kHalves * kps * Tile<KV, D>::bytes <= avail, "LDS budget");
+};
+
+// Slot (row of the K tile) that lane row m of M-block mb feeds into the QK
+// MFMA, so that accumulator element i of lane group g is slot 32g + 16mb + i.
+__device__ __forceinline__ int k_perm(int mb, int m) {
+  return 32 * ((m >> 2) & 1) + 16 * mb + 4 * (m >> 3) + (m & 3);
+}
+
+// XOR swizzles of 16-byte chunks against LDS bank conflicts.  K: the eight
+// lanes of a phase read slots {16mb + 0..3, 32 + 16mb + 0..3}.  V^T: they read
+// rows d .. d+7 at the same chunk.
+template <int KV, int D>
+__device__ __forceinline__ int k_swz(int slot) {
+  constexpr int cpr = Tile<KV, D>::k_cpr;
+  const int s = (slot & 3) | ((slot >> 3) & 4);
+  return cpr >= 8 ? s : (s & (cpr - 1));
+}
+template <int KV, int D>
+__device__ __forceinline__ int v_swz(int d) {
+  constexpr int cpr = Tile<KV, D>::v_cpr;
+  return cpr == 4 ? ((d >> 1) & 3) : (d & 7);
+}
+template <int KV, int D>
+__device__ __forceinline__ int k_addr(int slot, int c) {
+  return slot * Tile<KV, D>::k_row + ((c ^ k_swz<KV, D>(slot)) << 4);
+}
+template <int KV, int D>
+__device__ __forceinline__ int v_addr(int d, int c) {
+  return Tile<KV, D>::v_off + d * Tile<KV, D>::v_row + ((c ^ v_swz<KV, D>(d)) << 4);
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
+  // address-space conversions: generic -> global (1) and generic -> LDS (3)
+  __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(lds_wave_base), 16, 0, 0);
+}
+
+// Issue the direct-to-LDS loads of one tile for one key half.  Every wave of
+// the half moves whole 1 KB blocks (64 lanes x 16 bytes, contiguous in LDS);
+// each lane picks the global chunk that belongs at its LDS position.  Slots
+// past N read slot N-1 (finite data; such slots are masked by block -1).
+template <int KV, int D>
+__device__ __forceinline__ void load_tile(const AttnArgs& a, int h, int tile, uint8_t* buf, int wq, int lane) {
+  using T = Tile<KV, D>;
+  const int key0 = tile * kKT;
+#pragma unroll
+  for (int j = 0; j < T::k_instr; ++j) {
+    const int blk = wq * T::k_instr + j;
+    const int p = blk * kWave + lane;  // LDS chunk index
+    const int r = p / T::k_cpr, cp = p % T::k_cpr;
+    const int cl = cp ^ k_swz<KV, D>(r);
+    const int key = min(key0 + r, a.N - 1);
+    dma16(a.k + (static_cast<size_t>(h) * a.N + key) * T::k_row + cl * 16, buf + T::k_off + blk * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < T::v_instr; ++j) {
+    const int blk = wq * T::v_instr + j;
+    const int p = blk * kWave + lane;
+    const int d = p / T::v_cpr, cp = p % T::v_cpr;
+    const int cl = cp ^ v_swz<KV, D>(d);
+    dma16(a.v + ((static_cast<size_t>(h) * D + d) * a.v_ld + key0) * T::es + cl * 16,
+          buf + T::v_off + blk * 1024);
+  }
+  {
+    // per-slot metadata, one DMA instruction per wave so that every wave has
+    // the same number of loads in flight: FP8 moves 48 chunks (k_scale,
+    // v_scale, slot_block; 12 per wave), the other formats 16 (slot_block).
+    constexpr int per_wave = KV == KV_FP8 ? 12 : 4;
+    const int c = wq * per_wave + lane;  // chunk of the 768-byte raw area
+    const int base_chunk = KV == KV_FP8 ? 0 : 32;
+    if (lane < per_wave) {
+      const int cc = base_chunk + c, which = cc >> 4, j = (cc & 15) * 4;
+      const void* src = which == 0 ? static_cast<const void*>(a.k_scale + static_cast<size_t>(h) * a.v_ld + key0 + j)
+                        : which == 1 ? static_cast<const void*>(a.v_scale + static_cast<size_t>(h) * a.v_ld + key0 + j)
+                                     : static_cast<const void*>(a.slot_block + key0 + j);
+      dma16(src, buf + T::raw_off + (base_chunk + wq * per_wave) * 16);
+    }
+  }
+}
+
+template <int KV, int D>
+constexpr int dma_ops_per_tile() {
+  return Tile<KV, D>::k_instr + Tile<KV, D>::v_instr + 1;
+}
+
+// s_waitcnt vmcnt(N) as a real instruction (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima),
+// so that the compiler's own wait insertion accounts for it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding load, including tiles still in flight.
+// Callers wait for exactly what must be visible first.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Q operand registers of one lane (query n = lane % 32, group g = lane / 32).
+template <int KV, int D>
+struct QFrag;
+template <int D>
+struct QFrag<KV_FP8, D> {
+  v8i q[D / 64];
+};
+template <int D>
+struct QFrag<KV_BF16, D> {
+  v8bf q[D / 16];
+};
+template <int D>
+struct QFrag<KV_F32, D> {
+  float q[D / 2];
+};
+
+// d index of element e (0..D/2-1) held by lane group g in the Q operand.
+template <int KV, int D>
+__device__ __forceinline__ int q_dim(int g, int e) {
+  if constexpr (KV == KV_FP8) return (e / 32) * 64 + 32 * g + (e % 32);
+  else if constexpr (KV == KV_BF16) return (e / 8) * 16 + 8 * g + (e % 8);
+  else return 2 * e + g;
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+template <int KV, int D>
+__global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
+  using T = Tile<KV, D>;
+  constexpr int KPS = Stages<KV, D>::kps;
+  // One array per pipeline stage (kps tiles for each key half).  Separate
+  // objects let the compiler see that reading one stage does not depend on
+  // the loads still landing in the other, so it adds no waits of its own.
+  constexpr int kStageBytes = kHalves * KPS * T::bytes;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) float2 rope_tab[64 + 8 * 64 + 16 * 64];
+  __shared__ float red[kWaves];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int kh = wave / kQSub;  // key half
+  const int wq = wave % kQSub;  // query sub-tile (and wave index inside the half)
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // ---- work item
+  int item = blockIdx.x;
+  if (a.remap) item = (item % 8) * (gridDim.x / 8) + item / 8;
+  const int qt = item % a.n_qt;
+  const int hs = item / a.n_qt;
+  const int split = hs % a.n_splits;
+  const int h = hs / a.n_splits;
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
+  // local tile li of this half is tile t_begin + 2 li + kh; a step covers
+  // local tiles KPS*step .. KPS*step + KPS-1
+  const int n_local = (max(t_end - t_begin, 0) + 1) / 2;
+  const int n_steps = (n_local + KPS - 1) / KPS;
+  auto tile_of = [&](int li) { return t_begin + 2 * li + kh; };
+  auto has_tile = [&](int li) { return li < n_local && tile_of(li) < t_end; };
+  auto tile_buf = [&](uint8_t* stage, int kk) { return stage + (kh * KPS + kk) * T::bytes; };
+  // Every step issues KPS tiles' loads for every wave (past the end a valid
+  // tile is reloaded into a slot nobody reads), so wait counts are uniform.
+  auto issue_step = [&](uint8_t* stage, int st) {
+#pragma unroll
+    for (int kk = 0; kk < KPS; ++kk) {
+      const int li = st * KPS + kk;
+      load_tile<KV, D>(a, h, has_tile(li) ? tile_of(li) : t_begin, tile_buf(stage, kk), wq, lane);
+    }
+  };
+
+
+  // ---- queries of this lane
+  const int q_base = qt * kQT;
+  const int iq = wq * kQW + n;
+  const int qi = q_base + iq;
+  const bool q_ok = qi < a.n_q;
+  const int wave_q0 = q_base + wq * kQW;
+  const bool wave_active = wave_q0 < a.n_q;
+  const int wave_q1 = max(min(wave_q0 + kQW, a.n_q) - 1, wave_q0);
+  const int qb_lo = a.q_block0 + wave_q0 / a.q_block_len;
+  const int qb_hi = a.q_block0 + wave_q1 / a.q_block_len;
+  const int my_qb = a.q_block0 + (q_ok ? qi : wave_q0) / a.q_block_len;
+
+  // ---- raw Q of this lane, loaded before any tile so that waiting for it
+  //      does not wait for tiles in flight.  Lane group g holds half of the
+  //      query's d values in runs of even length (both members of every RoPE
+  //      pair) for FP8/BF16; for F32 every pair (2e, 2e+1).
+  constexpr int kQRaw = KV == KV_F32 ? D / 4 : D / 16;  // 16-byte loads per lane
+  v4u qraw[kQRaw];
+  {
+    const size_t qrow = (static_cast<size_t>(q_ok ? qi : 0) * a.H + h) * D;
+    const uint8_t* qb = static_cast<const uint8_t*>(a.q) + qrow * (KV == KV_F32 ? 4 : 2);
+#pragma unroll
+    for (int r = 0; r < kQRaw; ++r) {
+      int byte_off;
+      if constexpr (KV == KV_FP8) byte_off = ((r / 4) * 64 + 32 * g) * 2 + (r % 4) * 16;
+      else if constexpr (KV == KV_BF16) byte_off = (r * 16 + 8 * g) * 2;
+      else byte_off = r * 16;
+      qraw[r] = *reinterpret_cast<const v4u*>(qb + byte_off);
+    }
+  }
+
+  // ---- RoPE frequencies this thread needs for the angle tables below
+  constexpr int kRopeRows = 1 + 8 + 16;
+  constexpr int kRopePer = (kRopeRows * (D / 2) + kThreads - 1) / kThreads;
+  double rev[kRopePer];
+#pragma unroll
+  for (int k = 0; k < kRopePer; ++k) {
+    const int e = tid + k * kThreads;
+    rev[k] = (a.use_rope && e < kRopeRows * (D / 2)) ? a.rope.rev[e % (D / 2)] : 0.0;
+  }
+
+  // ---- start the first step's tiles
+  if (n_steps > 0) issue_step(st0, 0);
+  // ---- RoPE angle tables: e^{i pos theta_j} = e^{i P0 theta_j} e^{i 16 i1 theta_j} e^{i i0 theta_j}
+  //      for pos = P0 + 16 i1 + i0 (angles formed in float64 before sincos).
+  float2* rE0 = rope_tab;                                                   // [64]
+  float2* rE1 = rE0 + 64;                                                  // [8][64]
+  float2* rE2 = rE1 + 8 * 64;                                              // [16][64]
+  const long long P0 = static_cast<long long>(a.q_pos0) + q_base;
+  if (a.use_rope) {
+#pragma unroll
+    for (int k = 0; k < kRopePer; ++k) {
+      const int e = tid + k * kThreads;
+      if (e < kRopeRows * (D / 2)) {
+        const int row = e / (D / 2), j = e % (D / 2);
+        const long long pos = row == 0 ? P0 : (row <= 8 ? 16LL * (row - 1) : static_cast<long long>(row - 9));
+        float2 cs;
+        rope_cs_rev(rev[k], pos, &cs.x, &cs.y);
+        float2* dst = row == 0 ? rE0 + j : (row <= 8 ? rE1 + (row - 1) * 64 + j : rE2 + (row - 9) * 64 + j);
+        *dst = cs;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    bare_barrier();
+  }
+
+  // ---- Q: load, rotate, (quantise) into MFMA operand registers
+  QFrag<KV, D> qf;
+  float c_mul = a.scale_log2;  // y = c_mul * s_k * S + ...
+  {
+    float x[D / 2];
+    if constexpr (KV == KV_F32) {
+      // qraw holds (q[4r], q[4r+1], q[4r+2], q[4r+3]); element e is d = 2e + g
+#pragma unroll
+      for (int e = 0; e < D / 2; ++e) {
+        const v4u w = qraw[e / 2];
+        const float x0 = __uint_as_float((e & 1) ? w.z : w.x);
+        const float x1 = __uint_as_float((e & 1) ? w.w : w.y);
+        float y0 = x0, y1 = x1;
+        if (a.use_rope) {
+          const float2 r = cmul(cmul(rE0[e], rE1[(iq >> 4) * 64 + e]), rE2[(iq & 15) * 64 + e]);
+          y0 = x0 * r.x - x1 * r.y;
+          y1 = x0 * r.y + x1 * r.x;
+        }
+        x[e] = q_ok ? (g ? y1 : y0) : 0.f;
+      }
+    } else {
+      // qraw word k holds bf16 elements (2k, 2k+1) of this lane's run order
+#pragma unroll
+      for (int e = 0; e < D / 2; e += 2) {
+        const uint32_t w = qraw[e / 8][(e / 2) % 4];
+        const float x0 = __uint_as_float(w << 16);
+        const float x1 = __uint_as_float(w & 0xFFFF0000u);
+        float y0 = x0, y1 = x1;
+        if (a.use_rope) {
+          const int j = q_dim<KV, D>(g, e) >> 1;
+          const float2 r = cmul(cmul(rE0[j], rE1[(iq >> 4) * 64 + j]), rE2[(iq & 15) * 64 + j]);
+          y0 = x0 * r.x - x1 * r.y;
+          y1 = x0 * r.y + x1 * r.x;
+        }
+        x[e] = q_ok ? y0 : 0.f;
+        x[e + 1] = q_ok ? y1 : 0.f;
+      }
+    }
+    if constexpr (KV == KV_FP8) {
+      // one scale for the workgroup's 128 queries: s_q = max|q| / 448
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 2; ++e) am = fmaxf(am, fabsf(x[e]));
+      am = group_max<kWave>(am);
+      if (lane == 0) red[wave] = am;
+      __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      bare_barrier();
+      am = red[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) am = fmaxf(am, red[w]);
+      const float sq = am > 0.f ? am / 448.f : 1.f;
+      const float iq8 = am > 0.f ? 448.f / am : 0.f;
+      c_mul = a.scale_log2 * sq;
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int e = ks * 32 + 4 * w;
+          qf.q[ks][w] =
+              static_cast<int>(cvt_fp8x4(x[e] * iq8, x[e + 1] * iq8, x[e + 2] * iq8, x[e + 3] * iq8));
+        }
+      }
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf.q[ks][e] = static_cast<__bf16>(x[ks * 8 + e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / 2; ++e) qf.q[e] = x[e];
+    }
+  }
+
+  // ---- accumulators
+  v16f o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = v16f{};
+  float m_run = -INFINITY;  // stabiliser (log2 units)
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial sums of p
+
+  // Attention over one tile in LDS (skipped when no query of the wave sees it).
+  auto compute_tile = [&](const uint8_t* buf) {
+    const int kb = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512)[lane];
+    const bool kval = kb != -1;
+    if (__ballot(kval && kb <= qb_hi) == 0ull) return;
+    const bool all_vis = __ballot(!(kval && kb <= qb_lo)) == 0ull;
+    const bool all_hist = __ballot(!(kval && kb < qb_lo)) == 0ull;
+    const bool all_same = qb_lo == qb_hi && __ballot(!(kval && kb == qb_lo)) == 0ull;
+    // wave-uniform in an SGPR, so the branch below is a scalar branch
+    const int fast = __builtin_amdgcn_readfirstlane(all_vis && (all_hist || all_same || a.bias_log2 == 0.f));
+
+    // -- S^T = K Q^T: accumulator element i of lane group g is slot 32g + 16mb + i
+    v16f s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = v16f{};
+      const int slot = k_perm(mb, n);
+      if constexpr (KV == KV_FP8) {
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+          const int c0 = 4 * ks + 2 * g;
+          const v4i lo = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0));
+          const v4i hi = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0 + 1));
+          const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf.q[ks], s[mb], 0, 0, 0, 0, 0, 0);
+        }
+      } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const v8bf av = *reinterpret_cast<const v8bf*>(buf + k_addr<KV, D>(slot, 2 * ks + g));
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf.q[ks], s[mb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 2; ++ks) {
+          const int dd = 2 * ks + g;
+          const float av = *reinterpret_cast<const float*>(buf + k_addr<KV, D>(slot, dd >> 2) + (dd & 3) * 4);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, qf.q[ks], s[mb], 0, 0, 0);
+        }
+      }
+    }
+
+    // -- y = c s_k S + log2 s_v (+ bias2), masked to -inf
+    const float* kfc = reinterpret_cast<const float*>(buf + T::kfc_off);
+    const float* lvsel = reinterpret_cast<const float*>(buf + (all_hist ? T::lv1_off : T::lv0_off));
+    const float* lv0 = reinterpret_cast<const float*>(buf + T::lv0_off);
+    const float* lv1 = reinterpret_cast<const float*>(buf + T::lv1_off);
+    const int32_t* kbs = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512);
+    float tmax = -INFINITY;
+    if (fast) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int slot0 = 32 * g + 16 * mb + 4 * qq;
+          const v4f kf = *reinterpret_cast<const v4f*>(kfc + slot0);
+          const v4f lb = *reinterpret_cast<const v4f*>(lvsel + slot0);
+          s[mb][4 * qq + 0] = fmaf(s[mb][4 * qq + 0], kf.x, lb.x);
+          s[mb][4 * qq + 1] = fmaf(s[mb][4 * qq + 1], kf.y, lb.y);
+          s[mb][4 * qq + 2] = fmaf(s[mb][4 * qq + 2], kf.z, lb.z);
+          s[mb][4 * qq + 3] = fmaf(s[mb][4 * qq + 3], kf.w, lb.w);
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int slot0 = 32 * g + 16 * mb + 4 * qq;
+          const v4f kf = *reinterpret_cast<const v4f*>(kfc + slot0);
+          const v4f l0 = *reinterpret_cast<const v4f*>(lv0 + slot0);
+          const v4f l1 = *reinterpret_cast<const v4f*>(lv1 + slot0);
+          const v4i kb4 = *reinterpret_cast<const v4i*>(kbs + slot0);
+          const float kfa[4] = {kf.x, kf.y, kf.z, kf.w};
+          const float l0a[4] = {l0.x, l0.y, l0.z, l0.w}, l1a[4] = {l1.x, l1.y, l1.z, l1.w};
+          const int kba[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int cls = visibility_class(kba[r], my_qb);
+            const float y = fmaf(s[mb][4 * qq + r], kfa[r], cls == kVisBias ? l1a[r] : l0a[r]);
+            s[mb][4 * qq + r] = cls == kVisNone ? -INFINITY : y;
+          }
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float m8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m8[e] = fmaxf(s[mb][2 * e], s[mb][2 * e + 1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m8[e] = fmaxf(m8[e], m8[e + 4]);
+      tmax = fmaxf(tmax, fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])));
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (__ballot(tmax > m_run + kTau) != 0ull) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l_part[r] *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+
+    // -- P~ = 2^(y - m); l += P~ / s_v
+    const float* ivfp = reinterpret_cast<const float*>(buf + T::ivf_off);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const v4f iv = *reinterpret_cast<const v4f*>(ivfp + 32 * g + 16 * mb + 4 * qq);
+        const float iva[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[mb][4 * qq + r] - msub);
+          s[mb][4 * qq + r] = p;
+          l_part[r] = fmaf(p, iva[r], l_part[r]);
+        }
+      }
+    }
+
+    // -- O^T += V^T P^T (reduction index: slot 32g + j of the tile)
+    if constexpr (KV == KV_FP8) {
+      v8i pb;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          pb[4 * mb + qq] = static_cast<int>(
+              cvt_fp8x4(s[mb][4 * qq], s[mb][4 * qq + 1], s[mb][4 * qq + 2], s[mb][4 * qq + 3]));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + n;
+        const v4i lo = *reinterpret_cast<const v4i*>(buf + v_addr<KV, D>(d, 2 * g));
+        const v4i hi = *reinterpret_cast<const v4i*>(buf + v_addr<KV, D>(d, 2 * g + 1));
+        const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, o[db], 0, 0, 0, 0, 0, 0);
+      }
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        v8bf pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[st >> 1][8 * (st & 1) + e]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int d = 32 * db + n;
+          const v8bf av = *reinterpret_cast<const v8bf*>(buf + v_addr<KV, D>(d, 4 * g + st));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[db], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int slot = 32 * g + 16 * mb + e;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const int d = 32 * db + n;
+            const float av = *reinterpret_cast<const float*>(buf + v_addr<KV, D>(d, slot >> 2) + (slot & 3) * 4);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, s[mb][e], o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  // One pipeline step: the KPS tiles of stage `cur` are computed while the
+  // next step's tiles land in `nxt`.
+  auto step = [&](uint8_t* cur, uint8_t* nxt, int st) {
+    wait_vm<0>();    // this step's loads (issued one step ago) have landed
+    bare_barrier();  // B1: visible to all waves; every wave is done with `nxt`
+    if (st + 1 < n_steps) issue_step(nxt, st + 1);
+    if (wq == 0) {
+      // per-slot factors of each tile (one lane per slot)
+#pragma unroll
+      for (int kk = 0; kk < KPS; ++kk) {
+        if (!has_tile(st * KPS + kk)) continue;
+        uint8_t* buf = tile_buf(cur, kk);
+        const float* raw = reinterpret_cast<const float*>(buf + T::raw_off);
+        float kfc = c_mul, lv = 0.f, ivf = 1.f;
+        if constexpr (KV == KV_FP8) {
+          const float vs = fmaxf(raw[64 + lane], kMinVScale);
+          kfc = c_mul * raw[lane];
+          lv = __builtin_amdgcn_logf(vs);
+          ivf = __builtin_amdgcn_rcpf(vs);
+        }
+        reinterpret_cast<float*>(buf + T::kfc_off)[lane] = kfc;
+        reinterpret_cast<float*>(buf + T::lv0_off)[lane] = lv;
+        reinterpret_cast<float*>(buf + T::lv1_off)[lane] = lv + a.bias_log2;
+        reinterpret_cast<float*>(buf + T::ivf_off)[lane] = ivf;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    bare_barrier();  // B2: per-slot factors visible
+    // Already satisfied (this step's loads were waited for before B1); tells
+    // the compiler's wait analysis that only the next step's loads are in flight.
+    wait_vm<KPS * dma_ops_per_tile<KV, D>()>();
+    if (!wave_active) return;
+#pragma unroll
+    for (int kk = 0; kk < KPS; ++kk)
+      if (has_tile(st * KPS + kk)) compute_tile(tile_buf(cur, kk));
+  };
+  for (int st = 0; st < n_steps; st += 2) {
+    step(st0, st1, st);
+    if (st + 1 < n_steps) step(st1, st0, st + 1);
+  }
+
+  // ---- merge the two key halves of every query sub-tile through LDS
+  float l_sum = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
+  __syncthreads();  // all tiles consumed; stage buffers are free
+  static_assert(2 * kWave * (D / 2 + 2) * 4 <= kStageBytes, "merge buffer");
+  float* xch = (wq < 2 ? reinterpret_cast<float*>(st0) : reinterpret_cast<float*>(st1)) +
+               ((wq & 1) * kWave + lane) * (D / 2 + 2);
+  if (kh == 1) {
+    xch[0] = m_run;
+    xch[1] = l_sum;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xch[2 + 16 * b + e] = o[b][e];
+  }
+  __syncthreads();
+  if (kh == 1 || !wave_active) return;
+  {
+    const float m1 = xch[0], l1 = xch[1];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_sum = a0 * l_sum + a1 * l1;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[b][e] = a0 * o[b][e] + a1 * xch[2 + 16 * b + e];
+    m_run = mm;
+  }
+
+  // ---- epilogue
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_sum), __float_as_uint(l_sum), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const bool any = m_run != -INFINITY && l_tot > 0.f;
+  const float oscale = any ? 1.f / l_tot : 0.f;
+  const float lse_v = any ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!q_ok) return;
+  if (a.n_splits == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d = 32 * db + 8 * qq + 4 * g;
+        const size_t off = (static_cast<size_t>(qi) * a.H + h) * D + d;
+        const float r0 = o[db][4 * qq] * oscale, r1 = o[db][4 * qq + 1] * oscale;
+        const float r2 = o[db][4 * qq + 2] * oscale, r3 = o[db][4 * qq + 3] * oscale;
+        if constexpr (KV == KV_F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = make_float4(r0, r1, r2, r3);
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+              make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+        }
+      }
+    }
+    if (a.lse && g == 0) a.lse[static_cast<size_t>(h) * a.n_q + qi] = lse_v;
+  } else {
+    float* po = a.part_o + ((static_cast<size_t>(split) * a.n_q + qi) * a.H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d = 32 * db + 8 * qq + 4 * g;
+        *reinterpret_cast<float4*>(po + d) =
+            make_float4(o[db][4 * qq] * oscale, o[db][4 * qq + 1] * oscale, o[db][4 * qq + 2] * oscale,
+                        o[db][4 * qq + 3] * oscale);
+      }
+    if (g == 0) a.part_lse[(static_cast<size_t>(split) * a.H + h) * a.n_q + qi] = lse_v;
+  }
+}
+
+// Merge split partials (each normalised by its own sum) in fixed split order:
+// out = sum_s exp(lse_s - LSE) o_s,  LSE = ln sum_s exp(lse_s).
+template <int KV, int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* part_o, const float* part_lse,
+                                                      int n_splits, int n_q, int H, void* out,
+                                                      float* lse) {
+  const int row = blockIdx.x * (256 / 32) + threadIdx.x / 32;  // (query, head) row
+  const int lane = threadIdx.x % 32;
+  if (row >= n_q * H) return;
+  const int qi = row / H, h = row % H;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[(static_cast<size_t>(s) * H + h) * n_q + qi]);
+  float acc[D / 32];
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ls = part_lse[(static_cast<size_t>(s) * H + h) * n_q + qi];
+      const float w = ls == -INFINITY ? 0.f : __expf(ls - mx);
+      wsum += w;
+      const float* po = part_o + ((static_cast<size_t>(s) * n_q + qi) * H + h) * D;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) acc[e] += w * po[lane + 32 * e];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) {
+    const size_t off = static_cast<size_t>(row) * D + lane + 32 * e;
+    if constexpr (KV == KV_F32) static_cast<float*>(out)[off] = acc[e] * inv;
+    else static_cast<uint16_t*>(out)[off] = f32_to_bf16(acc[e] * inv);
+  }
+  if (lse && lane == 0) lse[static_cast<size_t>(h) * n_q + qi] = mx == -INFINITY ? -INFINITY : mx + logf(wsum);
+}
+
+__global__ __launch_bounds__(256) void visibility_kernel(const int32_t* slot_block, int N, int n_q,
+                                                         int q_block0, int q_block_len, uint8_t* mask) {
+  const size_t total = static_cast<size_t>(n_q) * N;
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < total; e += gridDim.x * 256ull) {
+    const int qi = static_cast<int>(e / N), s = static_cast<int>(e % N);
+    const int qb = q_block0 + qi / q_block_len;
+    mask[e] = static_cast<uint8_t>(visibility_class(slot_block[s], qb));
+  }
+}
+
+template <int KV, int D>
+hipError_t attn_impl(const RingView& r, const AttnCall& c, int splits, hipStream_t s) {
+  AttnArgs a{};
+  a.k = static_cast<const uint8_t*>(r.k);
+  a.v = static_cast<const uint8_t*>(r.v);
+  a.k_scale = r.k_scale;
+  a.v_scale = r.v_scale;
+  a.slot_block = r.slot_block;
+  a.N = r.N;
+  a.H = r.H;
+  a.v_ld = r.v_ld;
+  a.q = c.q;
+  a.n_q = c.n_q;
+  a.q_pos0 = c.q_pos0;
+  a.q_block0 = c.q_block0;
+  a.q_block_len = c.q_block_len;
+  const float sigma = c.softmax_scale != 0.f ? c.softmax_scale : 1.f / std::sqrt(static_cast<float>(r.d));
+  a.scale_log2 = sigma * kLog2e;
+  a.bias_log2 = c.cache_bias * kLog2e;
+  a.out = c.out;
+  a.lse = c.lse;
+  a.n_qt = (c.n_q + kQT - 1) / kQT;
+  a.n_tiles = (r.N + kKT - 1) / kKT;
+  a.n_splits = splits;
+  a.tiles_per_split = (a.n_tiles + splits - 1) / splits;
+  a.use_rope = r.rope_base > 0.f;
+  for (int j = 0; j < D / 2; ++j)
+    a.rope.rev[j] = a.use_rope ? std::pow(static_cast<double>(r.rope_base), -2.0 * j / D) / (2.0 * M_PI) : 0.0;
+  if (splits > 1) {
+    a.part_o = static_cast<float*>(c.workspace);
+    a.part_lse = a.part_o + static_cast<size_t>(splits) * c.n_q * r.H * D;
+  }
+  const int total = a.n_qt * r.H * splits;
+  a.remap = (total % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((chunk_attn_kernel<KV, D>), dim3(total), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int rows = c.n_q * r.H;
+  hipLaunchKernelGGL((combine_kernel<KV, D>), dim3((rows + 7) / 8), dim3(256), 0, s, a.part_o, a.part_lse,
+                     splits, c.n_q, r.H, c.out, c.lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_supported(int kv, int d) { return !(kv == KV_F32 && d == 128); }
+
+int attention_splits(const RingView& r, int n_q) {
+  const int n_qt = (n_q + kQT - 1) / kQT;
+  const int n_tiles = (r.N + kKT - 1) / kKT;
+  const int items = n_qt * r.H;
+  // Split the key range only when the grid is far below one workgroup per CU;
+  // each split keeps at least 4 tiles (2 per key half).
+  int splits = 1;
+  while (items * splits * 2 <= 256 && (splits * 2) * 4 <= n_tiles) splits *= 2;
+  return splits;
+}
+
+size_t attention_workspace_bytes(const RingView& r, int n_q) {
+  const int splits = attention_splits(r, n_q);
+  if (splits == 1) return 0;
+  return static_cast<size_t>(splits) * n_q * r.H * (r.d + 1) * sizeof(float);
+}
+
+hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStream_t s) {
+  int splits = attention_splits(r, c.n_q);
+  if (splits > 1 && (c.workspace == nullptr || c.workspace_bytes < attention_workspace_bytes(r, c.n_q)))
+    splits = 1;
+  switch (r.kv * 1000 + r.d) {
+    case KV_FP8 * 1000 + 128: return attn_impl<KV_FP8, 128>(r, c, splits, s);
+    case KV_FP8 * 1000 + 64: return attn_impl<KV_FP8, 64>(r, c, splits, s);
+    case KV_BF16 * 1000 + 128: return attn_impl<KV_BF16, 128>(r, c, splits, s);
+    case KV_BF16 * 1000 + 64: return attn_impl<KV_BF16, 64>(r, c, splits, s);
+    case KV_F32 * 1000 + 64: return attn_impl<KV_F32, 64>(r, c, splits, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
+                                   uint8_t* mask, hipStream_t s) {
+  const size_t total = static_cast<size_t>(n_q) * r.N;
+  const int blocks = static_cast<int>(std::min<size_t>((total + 255) / 256, 8192));
+  hipLaunchKernelGGL(visibility_kernel, dim3(blocks), dim3(256), 0, s, r.slot_block, r.N, n_q, q_block0,
+                     q_block_len, mask);
+  return hipGetLastError();
+}
+
+}  // namespace rc

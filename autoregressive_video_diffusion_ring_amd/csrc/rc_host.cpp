@@ -1,0 +1,233 @@
+// C ABI of the ring-cache library: argument and state checks, ring
+// bookkeeping on the host, kernel launches on the caller's stream.
+//
+// Ring bookkeeping (Runway Characters, abstract: a ring cache written once per
+// chunk): N slots, `head` the next slot to write, the n_hist committed history
+// tokens just before it.  A write of n tokens covers (head + i) mod N; it
+// evicts the oldest history slots it overwrites, so n_hist becomes
+// min(n_hist, N - n).  The chunk stays "current" (n_cur = n) through its
+// denoising passes, each of which writes the same slots again, until
+// rc_ring_advance commits it: head += n (mod N), n_hist += n, n_cur = 0.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/rc.h"
+#include "rc_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+rc_status fail(rc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rc_status fail(rc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+rc_status ok() {
+  g_err.clear();
+  return RC_OK;
+}
+
+rc_status hip_fail(hipError_t e, const char* what) {
+  return fail(RC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(int32_t dt) { return dt == RC_F32 ? 4 : (dt == RC_BF16 ? 2 : 1); }
+
+rc_status check_geometry(int32_t n_slots, int32_t n_heads, int32_t head_dim, int32_t kv_dtype) {
+  if (n_slots < 1) return fail(RC_ERR_ARG, "n_slots must be >= 1 (got %d)", n_slots);
+  if (n_slots > (1 << 24)) return fail(RC_ERR_ARG, "n_slots too large (%d)", n_slots);
+  if (n_heads < 1 || n_heads > 4096) return fail(RC_ERR_ARG, "n_heads must be in 1..4096 (got %d)", n_heads);
+  if (kv_dtype != RC_F32 && kv_dtype != RC_BF16 && kv_dtype != RC_FP8_E4M3)
+    return fail(RC_ERR_ARG, "unknown kv_dtype %d", kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RC_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  return RC_OK;
+}
+
+rc_status check_ring(const rc_ring* r) {
+  if (!r) return fail(RC_ERR_ARG, "ring is NULL");
+  rc_status st = check_geometry(r->n_slots, r->n_heads, r->head_dim, r->kv_dtype);
+  if (st != RC_OK) return st;
+  if (r->v_ld != rc_ring_v_ld(r->n_slots))
+    return fail(RC_ERR_ARG, "v_ld must be rc_ring_v_ld(n_slots) = %d (got %d)", rc_ring_v_ld(r->n_slots), r->v_ld);
+  if (!std::isfinite(r->rope_base) || r->rope_base < 0.f) return fail(RC_ERR_ARG, "rope_base must be >= 0");
+  if (!r->k || !r->v || !r->slot_pos || !r->slot_block) return fail(RC_ERR_ARG, "ring device pointer is NULL");
+  if (r->kv_dtype == RC_FP8_E4M3 && (!r->k_scale || !r->v_scale))
+    return fail(RC_ERR_ARG, "FP8 ring needs k_scale and v_scale");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(r->k) | reinterpret_cast<uintptr_t>(r->v);
+  if (al & 15u) return fail(RC_ERR_ARG, "k and v must be 16-byte aligned");
+  return RC_OK;
+}
+
+rc_status check_state(const rc_ring* r) {
+  const int N = r->n_slots;
+  if (r->head < 0 || r->head >= N || r->n_hist < 0 || r->n_cur < 0 || r->n_hist + r->n_cur > N)
+    return fail(RC_ERR_STATE, "ring host state is corrupt (head %d, n_hist %d, n_cur %d, N %d)", r->head,
+                r->n_hist, r->n_cur, N);
+  return RC_OK;
+}
+
+rc::RingView view(const rc_ring* r) {
+  rc::RingView v{};
+  v.N = r->n_slots;
+  v.H = r->n_heads;
+  v.d = r->head_dim;
+  v.kv = r->kv_dtype;
+  v.v_ld = r->v_ld;
+  v.rope_base = r->rope_base;
+  v.k = r->k;
+  v.v = r->v;
+  v.k_scale = r->k_scale;
+  v.v_scale = r->v_scale;
+  v.slot_pos = r->slot_pos;
+  v.slot_block = r->slot_block;
+  return v;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t rc_ring_v_ld(int32_t n_slots) {
+  if (n_slots < 1) return 0;
+  return (n_slots + 63) / 64 * 64;
+}
+
+rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int32_t kv_dtype, size_t out[6]) {
+  if (!out) return fail(RC_ERR_ARG, "out is NULL");
+  rc_status st = check_geometry(n_slots, n_heads, head_dim, kv_dtype);
+  if (st != RC_OK) return st;
+  const size_t es = elem_size(kv_dtype);
+  out[0] = static_cast<size_t>(n_heads) * n_slots * head_dim * es;
+  out[1] = static_cast<size_t>(n_heads) * head_dim * rc_ring_v_ld(n_slots) * es;
+  const size_t ld = rc_ring_v_ld(n_slots);
+  out[2] = out[3] = kv_dtype == RC_FP8_E4M3 ? static_cast<size_t>(n_heads) * ld * sizeof(float) : 0;
+  out[4] = out[5] = ld * sizeof(int32_t);
+  return ok();
+}
+
+rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if (first_slot < 0 || first_slot >= r->n_slots)
+    return fail(RC_ERR_ARG, "first_slot must be in 0..%d (got %d)", r->n_slots - 1, first_slot);
+  hipError_t e = rc::launch_ring_clear(view(r), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "ring clear");
+  r->head = first_slot;
+  r->n_hist = 0;
+  r->n_cur = 0;
+  r->cur_pos0 = 0;
+  r->cur_block = 0;
+  return ok();
+}
+
+rc_status rc_cache_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0,
+                         int32_t block_id, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if ((st = check_state(r)) != RC_OK) return st;
+  if (!k_new || !v_new) return fail(RC_ERR_ARG, "k_new / v_new is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
+    return fail(RC_ERR_ARG, "k_new and v_new must be 16-byte aligned");
+  if (n_new < 1 || n_new > r->n_slots)
+    return fail(RC_ERR_ARG, "n_new must be in 1..%d (got %d)", r->n_slots, n_new);
+  if (block_id < 0) return fail(RC_ERR_ARG, "block_id must be >= 0 (got %d)", block_id);
+  if (static_cast<long long>(pos0) + n_new - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (r->n_cur > 0 && (n_new != r->n_cur || pos0 != r->cur_pos0 || block_id != r->cur_block))
+    return fail(RC_ERR_STATE,
+                "chunk (n %d, pos0 %d, block %d) is current; a rewrite must repeat it (got n %d, pos0 %d, block %d)",
+                r->n_cur, r->cur_pos0, r->cur_block, n_new, pos0, block_id);
+  hipError_t e = rc::launch_cache_write(view(r), k_new, v_new, n_new, r->head, pos0, block_id, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache write");
+  if (r->n_cur == 0) r->n_hist = std::min(r->n_hist, r->n_slots - n_new);
+  r->n_cur = n_new;
+  r->cur_pos0 = pos0;
+  r->cur_block = block_id;
+  return ok();
+}
+
+rc_status rc_cache_rerotate(rc_ring* r, int32_t delta, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if ((st = check_state(r)) != RC_OK) return st;
+  if (!(r->rope_base > 0.f)) return fail(RC_ERR_ARG, "rerotate needs a ring with RoPE (rope_base > 0)");
+  if (r->n_cur > 0 && (static_cast<long long>(r->cur_pos0) + delta < INT32_MIN ||
+                       static_cast<long long>(r->cur_pos0) + delta + r->n_cur > INT32_MAX))
+    return fail(RC_ERR_ARG, "positions overflow int32");
+  hipError_t e = rc::launch_rerotate(view(r), delta, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "rerotate");
+  if (r->n_cur > 0) r->cur_pos0 += delta;
+  return ok();
+}
+
+size_t rc_attention_workspace_bytes(const rc_ring* r, int32_t n_q) {
+  if (check_ring(r) != RC_OK || n_q < 1) return 0;
+  return rc::attention_workspace_bytes(view(r), n_q);
+}
+
+rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                             int32_t q_block_len, float cache_bias, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if (!q || !out) return fail(RC_ERR_ARG, "q / out is NULL");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15u)
+    return fail(RC_ERR_ARG, "q and out must be 16-byte aligned");
+  if (n_q < 1) return fail(RC_ERR_ARG, "n_q must be >= 1 (got %d)", n_q);
+  if (q_block_len < 1) return fail(RC_ERR_ARG, "q_block_len must be >= 1 (got %d)", q_block_len);
+  if (static_cast<long long>(q_pos0) + n_q - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (!std::isfinite(cache_bias) && !(cache_bias < 0.f))
+    return fail(RC_ERR_ARG, "cache_bias must be finite or -inf");
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(RC_ERR_ARG, "softmax_scale must be finite and >= 0");
+  if (workspace_bytes > 0 && !workspace) return fail(RC_ERR_ARG, "workspace_bytes > 0 with a NULL workspace");
+  rc::AttnCall c{q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, out, lse, workspace,
+                 workspace_bytes};
+  hipError_t e = rc::launch_chunk_attention(view(r), c, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk attention");
+  return ok();
+}
+
+rc_status rc_ring_advance(rc_ring* r, int32_t n) {
+  if (!r) return fail(RC_ERR_ARG, "ring is NULL");
+  rc_status st = check_state(r);
+  if (st != RC_OK) return st;
+  if (r->n_cur == 0 || n != r->n_cur)
+    return fail(RC_ERR_STATE, "advance(%d) needs n == n_cur > 0 (n_cur %d)", n, r->n_cur);
+  r->head = (r->head + n) % r->n_slots;
+  r->n_hist = std::min(r->n_hist + n, r->n_slots);
+  r->n_cur = 0;
+  return ok();
+}
+
+rc_status rc_debug_visibility(const rc_ring* r, int32_t n_q, int32_t q_block0, int32_t q_block_len, uint8_t* mask,
+                              void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if (!mask) return fail(RC_ERR_ARG, "mask is NULL");
+  if (n_q < 1 || q_block_len < 1) return fail(RC_ERR_ARG, "n_q and q_block_len must be >= 1");
+  hipError_t e = rc::launch_debug_visibility(view(r), n_q, q_block0, q_block_len, mask, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "visibility");
+  return ok();
+}
+
+const char* rc_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

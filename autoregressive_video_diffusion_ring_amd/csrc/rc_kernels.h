@@ -1,0 +1,50 @@
+// Internal interface between the C ABI (rc_host.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rc {
+
+// Plain copy of a ring's geometry and device pointers, as the kernels see it.
+struct RingView {
+  int N, H, d, kv, v_ld;
+  float rope_base;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  int32_t* slot_pos;
+  int32_t* slot_block;
+};
+
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+hipError_t launch_ring_clear(const RingView& r, hipStream_t s);
+
+// Writes n_new tokens to slots (head + i) mod N.
+hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* v_new, int n_new,
+                              int head, int pos0, int block_id, hipStream_t s);
+
+hipError_t launch_rerotate(const RingView& r, int delta, hipStream_t s);
+
+struct AttnCall {
+  const void* q;
+  int n_q, q_pos0, q_block0, q_block_len;
+  float cache_bias, softmax_scale;
+  void* out;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+// Number of key splits the attention uses for n_q queries (1 = none).
+int attention_splits(const RingView& r, int n_q);
+size_t attention_workspace_bytes(const RingView& r, int n_q);
+hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStream_t s);
+
+hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
+                                   uint8_t* mask, hipStream_t s);
+
+}  // namespace rc

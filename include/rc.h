@@ -1,0 +1,186 @@
+/*
+ * rc.h -- ring-cache chunk attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  It implements the attention hot path
+ * of streaming autoregressive video diffusion as described in "Runway
+ * Characters: Serving a 57B Video Diffusion Transformer for Real-Time
+ * Conversation" (abstract): every chunk's new keys and values are written
+ * once into a circular (ring) KV cache, with RoPE and FP8 quantisation applied
+ * at write time, the cached keys are given a delta rotation when positions are
+ * reset, and the chunk's queries attend over the whole cache on every call.
+ * The attention adds a scalar cache bias to the logits of earlier blocks (the
+ * "plastic window" of the video-conductor page, "Plastic Windows") and is
+ * block-causal: full inside a block, backward-only across blocks (StreamLTX
+ * project page, Training; "Why Live Video Generation Still Struggles With
+ * Timing", transcript).
+ *
+ * Conventions shared by every call:
+ *  - Device pointers point to GPU memory owned by the caller.  The library
+ *    never allocates, frees or synchronises, and keeps no pointer after a call
+ *    returns (the rc_ring struct holds the caller's pointers).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every device
+ *    call is asynchronous on that stream.
+ *  - Every argument and state check runs before anything is enqueued.  On a
+ *    non-OK return nothing was enqueued and the host state in the rc_ring is
+ *    unchanged; rc_last_error() describes the failure.  RC_ERR_HIP reports an
+ *    error from the HIP runtime when enqueuing.
+ *  - One ring is used from one host thread / stream at a time; there is no
+ *    internal locking.  NaN or Inf inputs are outside the contract.
+ */
+#ifndef RC_H_
+#define RC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RC_OK = 0,
+  RC_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, bad dtype) */
+  RC_ERR_UNSUPPORTED = 2,  /* valid but not built (e.g. head_dim other than 64/128) */
+  RC_ERR_STATE = 3,        /* call not allowed by the ring's host state */
+  RC_ERR_HIP = 4           /* the HIP runtime reported an error */
+} rc_status;
+
+typedef enum {
+  RC_F32 = 0,      /* float32 K and V                                  */
+  RC_BF16 = 1,     /* bfloat16 K and V                                 */
+  RC_FP8_E4M3 = 2  /* OCP e4m3fn codes (max 448) + float32 scales      */
+} rc_dtype;
+
+/*
+ * One layer's ring cache.  The caller fills the geometry and the device
+ * pointers, then calls rc_ring_init, which sets the host state.
+ *
+ * Device layout (sizes from rc_ring_sizes):
+ *   k          [H][N][d]        kv_dtype; row (h, s) is slot s of head h
+ *   v          [H][d][v_ld]     kv_dtype, TRANSPOSED: v[h][j][s] is element
+ *                               j of slot s; v_ld = rc_ring_v_ld(N) >= N
+ *   k_scale    [H][v_ld] float  FP8 only: k = code * k_scale[h][s]
+ *   v_scale    [H][v_ld] float  FP8 only: v = code * v_scale[h][s]
+ *   slot_pos   [v_ld]   int32   token position of each slot
+ *   slot_block [v_ld]   int32   block id of each slot, -1 = never written
+ * Entries s in [N, v_ld) are padding: the kernels read them as empty slots
+ * (block -1, scale 0, V 0) and never write them.
+ * Host state (maintained by the library; read it, do not write it):
+ *   head       next slot to write
+ *   n_hist     committed history tokens in the cache
+ *   n_cur      tokens of the current, not yet committed, chunk (0 = none)
+ *   cur_pos0, cur_block   position of the current chunk's first token, its block
+ */
+typedef struct rc_ring {
+  int32_t n_slots;     /* N >= 1 */
+  int32_t n_heads;     /* H >= 1 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t kv_dtype;    /* rc_dtype */
+  float rope_base;     /* RoPE base (10000 on the pages' workloads); 0 = no RoPE */
+  int32_t v_ld;        /* must equal rc_ring_v_ld(n_slots) */
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  int32_t* slot_pos;
+  int32_t* slot_block;
+  int32_t head, n_hist, n_cur, cur_pos0, cur_block;
+} rc_ring;
+
+/* Leading dimension of the transposed V buffer: N rounded up to 64. */
+int32_t rc_ring_v_ld(int32_t n_slots);
+
+/*
+ * Byte sizes of the six device buffers of a ring, written to out[0..5] in the
+ * order k, v, k_scale, v_scale, slot_pos, slot_block (scales are 0 unless
+ * FP8).  Returns RC_ERR_ARG / RC_ERR_UNSUPPORTED for a bad geometry.
+ */
+rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int32_t kv_dtype,
+                        size_t out[6]);
+
+/*
+ * Validate the geometry and pointers, zero K, V and the scales, set every
+ * slot_block to -1 and slot_pos to 0 (asynchronously on `stream`), and set the
+ * host state: head = first_slot (0 <= first_slot < N), n_hist = n_cur = 0.
+ */
+rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
+
+/*
+ * Write n_new tokens into slots (head + i) mod N, i < n_new (Runway
+ * Characters, abstract: ring cache, RoPE and FP8 quantisation once per write).
+ *   k_new, v_new  device [n_new][H][d], bfloat16 (float32 for an RC_F32 ring),
+ *                 token-major as a QKV projection produces them
+ *   pos0          position of token 0; token i has position pos0 + i
+ *   block_id      block id (>= 0) recorded for every written slot
+ * K is rotated by RoPE at its position; for FP8 rings each (head, token)
+ * vector of K and of V is quantised with scale = max|x| / 448 (float32) and
+ * codes = round-to-nearest-even(x / scale); for BF16 rings the values are
+ * rounded to bfloat16.  slot_pos and slot_block are set for the written slots.
+ * History slots overwritten by the write are evicted: n_hist becomes
+ * min(n_hist, N - n_new).  Every denoising pass of one chunk writes again
+ * before rc_ring_advance: while n_cur > 0, n_new, pos0 and block_id must repeat
+ * the current chunk's, else RC_ERR_STATE.  Requires 1 <= n_new <= N.
+ */
+rc_status rc_cache_write(rc_ring* ring, const void* k_new, const void* v_new, int32_t n_new,
+                         int32_t pos0, int32_t block_id, void* stream);
+
+/*
+ * Position reset (Runway Characters, abstract: a delta rotation when
+ * positions reset).  Every slot with slot_block != -1 (history and the current
+ * chunk) has its key rotated by delta: FP8 codes are dequantised, rotated,
+ * and quantised again with a fresh absmax scale.  slot_pos += delta for those
+ * slots, and cur_pos0 += delta when a chunk is current.  V is untouched.
+ * Requires rope_base > 0.
+ */
+rc_status rc_cache_rerotate(rc_ring* ring, int32_t delta, void* stream);
+
+/*
+ * Block-causal chunk attention of n_q queries over every cached slot.
+ *   q            device [n_q][H][d], bfloat16 (float32 for an RC_F32 ring),
+ *                not yet rotated; query i has position q_pos0 + i and block
+ *                q_block0 + i / q_block_len
+ *   cache_bias   added to the scaled logit of every visible slot whose block
+ *                is earlier than the query's (the plastic-window bias)
+ *   softmax_scale  logit scale; 0 means 1/sqrt(d)
+ *   out          device [n_q][H][d], same dtype as q
+ *   lse          device [H][n_q] float32 natural-log sum of exp of the logits,
+ *                or NULL
+ *   workspace    device scratch of workspace_bytes (may be NULL / 0); more
+ *                workspace lets the call split the key range over more
+ *                workgroups when n_q is small
+ * Slot s is visible to query i iff slot_block[s] != -1 and
+ * slot_block[s] <= block(i).  logit = scale * (RoPE(q_i) . k_s) +
+ * cache_bias * [slot_block[s] < block(i)].  A query that sees no slot gets
+ * out = 0 and lse = -inf.  Requires n_q >= 1 and q_block_len >= 1.
+ */
+rc_status rc_chunk_attention(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0,
+                             int32_t q_block0, int32_t q_block_len, float cache_bias,
+                             float softmax_scale, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace that lets rc_chunk_attention use its full key split for n_q queries. */
+size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
+
+/*
+ * Commit the current chunk as history (host only, nothing is enqueued):
+ * head = (head + n) mod N, n_hist += n, n_cur = 0.  Requires n == n_cur > 0.
+ */
+rc_status rc_ring_advance(rc_ring* ring, int32_t n);
+
+/*
+ * The visibility predicate used inside rc_chunk_attention, exported for
+ * checking: mask[i][s] (device uint8 [n_q][N]) = 0 if slot s is invisible to
+ * query i, 1 if visible without the bias (same block), 2 if visible with the
+ * bias (earlier block).
+ */
+rc_status rc_debug_visibility(const rc_ring* ring, int32_t n_q, int32_t q_block0,
+                              int32_t q_block_len, uint8_t* mask, void* stream);
+
+/* Thread-local description of the last error (empty string if none). */
+const char* rc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RC_H_ */

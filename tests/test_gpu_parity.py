@@ -1,0 +1,376 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case uses seeded synthetic N(0,1) inputs (synthetic_inputs.py) with the
+workload shapes: the tiny case, one streaming layer (757 new over 5,788 fp8
+slots, 40 heads, d 128), ring wrap + position reset, and joint audio-video
+block-causal attention (bf16, 32 heads).  Bookkeeping and masks must be
+bit-exact, FP8 codes within one step, attention within the tolerances in
+gpu_helpers.ATTN_TOL.  Attention is compared with the oracle fed the GPU's
+own cache contents (so write rounding is not counted twice) and, end to end,
+with the oracle's own cache.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_video_diffusion_ring_amd import RcError, Ring
+from oracle import e4m3
+from oracle.attention import ring_attention, visibility, query_blocks
+from oracle.ring import Ring as OracleRing
+from synthetic_inputs import WORKLOADS
+
+from gpu_helpers import (DEV, assert_attention_close, compare_cache, gpu_cache, inputs, oracle_from_gpu,
+                         oracle_rows, rel_l2, to_np64)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU", allow_module_level=True)
+
+
+def banner(msg):
+    print(f"\n[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def make_pair(N, H, d, kv, rope, first_slot=0):
+    return (Ring(N, H, d, kv, rope, first_slot=first_slot, device=DEV),
+            OracleRing(N, H, d, kv, rope, first_slot=first_slot))
+
+
+def write_both(g, o, rng, n, pos0, blk):
+    kt, k = inputs(rng, g.kv_name, (n, g.H, g.d))
+    vt, v = inputs(rng, g.kv_name, (n, g.H, g.d))
+    g.write(kt, vt, pos0, blk)
+    o.write(k, v, n, pos0, blk)
+    return kt, vt
+
+
+# ------------------------------------------------------------------ tiny
+def test_tiny_end_to_end():
+    w = WORKLOADS["tiny"]
+    banner("tiny: f32 ring N=96 H=2 d=64, 4 blocks of 32, bias -0.5")
+    rng = np.random.default_rng(w.seed)
+    B = w.extra["block_len"]
+    g, o = make_pair(w.n_slots, w.heads, w.head_dim, w.kv_dtype, w.rope_base)
+    for b in range(4):
+        write_both(g, o, rng, B, B * b, b)
+        if b < 3:
+            g.advance(B)
+            o.advance(B)
+    qt, q = inputs(rng, "f32", (B, w.heads, w.head_dim))
+    lse = torch.empty((w.heads, B), dtype=torch.float32, device=DEV)
+    out = g.attention(qt, 96, 3, B, w.cache_bias, lse=lse)
+    compare_cache(gpu_cache(g), o, "f32")
+    ref_gpu, lse_gpu_ref = ring_attention(oracle_from_gpu(g, w.rope_base), q, 96, 3, B, w.cache_bias)
+    assert_attention_close(out, ref_gpu, "f32")
+    assert np.max(np.abs(to_np64(lse) - lse_gpu_ref)) < 1e-5
+    ref, _ = ring_attention(o, q, 96, 3, B, w.cache_bias)
+    assert_attention_close(out, ref, "f32")
+
+
+# ------------------------------------------------------------------ writes
+def stream_ring(seed, head0=0, H=40, d=128, N=5788, n_hist=5031, n_new=757):
+    """History of n_hist tokens (block 0, positions 0..n_hist-1) committed,
+    then the current chunk of n_new tokens (block 1) written."""
+    rng = np.random.default_rng(seed)
+    g, o = make_pair(N, H, d, "fp8", 10000.0, first_slot=head0)
+    write_both(g, o, rng, n_hist, 0, 0)
+    g.advance(n_hist)
+    o.advance(n_hist)
+    write_both(g, o, rng, n_new, n_hist, 1)
+    return g, o, rng
+
+
+def test_write_stream_full_size():
+    banner("write: fp8 N=5788 H=40 d=128, 5031 history + 757 current")
+    g, o, _ = stream_ring(WORKLOADS["stream"].seed)
+    compare_cache(gpu_cache(g), o, "fp8")
+
+
+@pytest.mark.parametrize("head0", [4000, 5400])
+def test_write_wrap_and_rewrite(head0):
+    banner(f"write: wrap at head {head0}, then a second pass over the same chunk")
+    rng = np.random.default_rng(WORKLOADS["wrap"].seed)
+    N, H, d = 5788, 40, 128
+    g, o = make_pair(N, H, d, "fp8", 10000.0, first_slot=head0)
+    write_both(g, o, rng, 757, 5031, 1)
+    compare_cache(gpu_cache(g), o, "fp8")
+    # second denoising pass: new values, same slots, same state
+    write_both(g, o, rng, 757, 5031, 1)
+    c = gpu_cache(g)
+    compare_cache(c, o, "fp8")
+    slots = (head0 + np.arange(757)) % N
+    assert set(np.nonzero(c["slot_block"] == 1)[0]) == set(slots)
+    with pytest.raises(RcError):
+        g.write(*(inputs(rng, "fp8", (757, H, d))[0] for _ in range(2)), 5032, 1)
+    assert g.state() == o.state()
+
+
+@pytest.mark.parametrize("kv,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("fp8", 64)])
+def test_write_other_formats(kv, d):
+    banner(f"write: {kv} d={d} ragged chunks with wrap")
+    rng = np.random.default_rng(11)
+    N, H = 200, 3
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=170)
+    write_both(g, o, rng, 77, 1000, 0)
+    g.advance(77)
+    o.advance(77)
+    write_both(g, o, rng, 150, 1077, 1)
+    compare_cache(gpu_cache(g), o, kv)
+
+
+# ------------------------------------------------------------------ rerotate
+def test_rerotate_wrap_reset():
+    banner("rerotate: head 5400 (wrapped current chunk), delta -3000 over all slots")
+    head0 = (5400 - 5031) % 5788
+    g, o, rng = stream_ring(WORKLOADS["wrap"].seed, head0=head0)
+    # the current chunk starts at slot 5400 and wraps
+    assert g.state()[0] == 5400
+    before = oracle_from_gpu(g, 10000.0)
+    g.rerotate(-3000)
+    before.rerotate(-3000)
+    compare_cache(gpu_cache(g), before, "fp8")
+    # against re-encoding from scratch: dequantised keys within two steps
+    o.rerotate(-3000)
+    fresh = OracleRing(5788, 40, 128, "fp8", 10000.0, first_slot=head0)
+    rng2 = np.random.default_rng(WORKLOADS["wrap"].seed)
+    from gpu_helpers import inputs as _inp  # same draws as stream_ring
+    _, k0 = _inp(rng2, "fp8", (5031, 40, 128))
+    _, v0 = _inp(rng2, "fp8", (5031, 40, 128))
+    fresh.write(k0, v0, 5031, -3000, 0)
+    fresh.advance(5031)
+    _, k1 = _inp(rng2, "fp8", (757, 40, 128))
+    _, v1 = _inp(rng2, "fp8", (757, 40, 128))
+    fresh.write(k1, v1, 757, 5031 - 3000, 1)
+    gk = oracle_from_gpu(g, 10000.0).k_values()
+    s = np.maximum(fresh.k_scale, gpu_cache(g)["k_scale"]).astype(np.float64)[..., None]
+    assert np.all(np.abs(gk - fresh.k_values()) <= 3 * 16 * math.sqrt(2) * s)
+    assert g.state() == fresh.state()
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("kv,d", [("fp8", 128), ("fp8", 64), ("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_attention_ragged_multiblock(kv, d):
+    """Several tiles and a ragged tail on both axes, a wrapped ring with empty
+    slots, multi-block queries (block-causal) and a nonzero bias."""
+    banner(f"attention: {kv} d={d} N=300 H=3, 150 queries in 3 blocks, bias -0.5")
+    rng = np.random.default_rng(21)
+    N, H = 300, 3
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=250)
+    for b, (n, p0) in enumerate([(60, 1000), (70, 1060), (50, 1130)]):
+        write_both(g, o, rng, n, p0, b)
+        g.advance(n)
+        o.advance(n)
+    # queries: blocks 1..3, 50 each; block 3 has no keys of its own
+    qt, q = inputs(rng, kv, (150, H, d))
+    lse = torch.empty((H, 150), dtype=torch.float32, device=DEV)
+    out = g.attention(qt, 1060, 1, 50, -0.5, lse=lse)
+    ref, ref_lse = ring_attention(oracle_from_gpu(g, 10000.0), q, 1060, 1, 50, -0.5)
+    assert_attention_close(out, ref, kv)
+    lse_tol = {"fp8": 5e-2, "bf16": 2e-2, "f32": 1e-5}[kv]
+    assert np.max(np.abs(to_np64(lse) - ref_lse)) < lse_tol
+    ref2, _ = ring_attention(o, q, 1060, 1, 50, -0.5)
+    assert_attention_close(out, ref2, kv)
+
+
+def test_attention_stream_full_size_sampled():
+    banner("attention: streaming layer 757 x 5788 fp8, 40 heads, sampled rows")
+    g, o, rng = stream_ring(WORKLOADS["stream"].seed)
+    qt, q = inputs(rng, "fp8", (757, 40, 128))
+    lse = torch.empty((40, 757), dtype=torch.float32, device=DEV)
+    out = g.attention(qt, 5031, 1, 757, 0.0, lse=lse)
+    rows = np.r_[0:757:9, 750:757]
+    ref, ref_lse = oracle_rows(oracle_from_gpu(g, 10000.0), q, rows, 5031, 1, 757, 0.0)
+    assert_attention_close(out, ref, "fp8", rows=rows)
+    assert np.max(np.abs(to_np64(lse)[:, rows] - ref_lse)) < 5e-2
+    # determinism: the same call twice gives identical bits
+    out2 = g.attention(qt, 5031, 1, 757, 0.0)
+    assert torch.equal(out, out2)
+
+
+def test_attention_after_reset_matches_before():
+    """RoPE makes attention depend on relative positions only: after a reset
+    by delta, queries moved by the same delta give the same result (within
+    the FP8 re-quantisation of the keys)."""
+    banner("attention: before vs after rerotate(-3000) with rebased queries")
+    g, o, rng = stream_ring(7, H=8, N=1000, n_hist=700, n_new=200)
+    qt, q = inputs(rng, "fp8", (200, 8, 128))
+    a = to_np64(g.attention(qt, 700, 1, 200, -0.5))
+    g.rerotate(-3000)
+    b = to_np64(g.attention(qt, 700 - 3000, 1, 200, -0.5))
+    assert_attention_close(b, a, "fp8")
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, -2300, 1, 200, -0.5)
+    assert_attention_close(b, ref, "fp8")
+
+
+def test_zero_query_closed_form():
+    banner("attention: Q = 0 closed form (pins bias and visibility)")
+    g, o, rng = stream_ring(8, H=4, N=700, n_hist=500, n_new=150)
+    beta = -0.7
+    q = torch.zeros((150, 4, 128), dtype=torch.bfloat16, device=DEV)
+    out = to_np64(g.attention(q, 500, 1, 150, beta))
+    orc = oracle_from_gpu(g, 10000.0)
+    V = orc.v_values()
+    hist, cur = orc.slot_block == 0, orc.slot_block == 1
+    num = math.exp(beta) * V[:, hist].sum(1) + V[:, cur].sum(1)
+    den = math.exp(beta) * hist.sum() + cur.sum()
+    closed = np.broadcast_to((num / den)[None], out.shape)
+    assert_attention_close(out, closed, "fp8")
+
+
+def test_slot_permutation_invariance():
+    banner("attention: permuting physical slots (with positions and blocks) changes nothing")
+    g, o, rng = stream_ring(9, H=4, N=640, n_hist=500, n_new=100)
+    qt, q = inputs(rng, "fp8", (100, 4, 128))
+    a = to_np64(g.attention(qt, 500, 1, 100, -0.5))
+    perm = torch.from_numpy(np.random.default_rng(2).permutation(640)).to(DEV)
+    H, N, d = 4, 640, 128
+    kb = g.buffers[0].view(H, N, d)
+    kb.copy_(kb[:, perm].clone())
+    vb = g.buffers[1].view(H, d, g.v_ld)
+    vb[:, :, :N] = vb[:, :, :N][:, :, perm].clone()
+    for i in (2, 3):
+        sb = g.buffers[i].view(torch.float32)[:H * g.v_ld].view(H, g.v_ld)[:, :N]
+        sb.copy_(sb[:, perm].clone())
+    for i in (4, 5):
+        mb = g.buffers[i].view(torch.int32)[:N]
+        mb.copy_(mb[perm].clone())
+    b = to_np64(g.attention(qt, 500, 1, 100, -0.5))
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 500, 1, 100, -0.5)
+    assert_attention_close(a, ref, "fp8")
+    assert_attention_close(b, ref, "fp8")
+    # two independent FP8 roundings of P (different tile compositions)
+    assert rel_l2(b, a) < 6e-2
+
+
+def test_rows_without_visible_keys():
+    banner("attention: queries of a block before every cached block")
+    rng = np.random.default_rng(5)
+    g, o = make_pair(128, 2, 128, "bf16", 0.0)
+    write_both(g, o, rng, 100, 0, 5)
+    qt, _ = inputs(rng, "bf16", (40, 2, 128))
+    lse = torch.empty((2, 40), dtype=torch.float32, device=DEV)
+    out = g.attention(qt, 0, 3, 20, 0.0, lse=lse)  # blocks 3 and 4: nothing visible
+    assert torch.count_nonzero(out) == 0
+    assert torch.all(torch.isneginf(lse))
+
+
+# ------------------------------------------------------------------ joint A/V
+def av_rings(seed):
+    w = WORKLOADS["av"]
+    rng = np.random.default_rng(seed)
+    H, d, B = w.heads, w.head_dim, w.extra["blocks"]
+    vb, ab = w.extra["video_block"], w.extra["audio_block"]
+    gv, ov = make_pair(vb * B, H, d, "bf16", 0.0)
+    ga, oa = make_pair(ab * B, H, d, "bf16", 0.0)
+    for b in range(B):
+        write_both(gv, ov, rng, vb, vb * b, b)
+        write_both(ga, oa, rng, ab, ab * b, b)
+        if b < B - 1:
+            for r in (gv, ov, ga, oa):
+                r.advance(vb if r in (gv, ov) else ab)
+    qv = inputs(rng, "bf16", (vb * B, H, d))
+    qa = inputs(rng, "bf16", (ab * B, H, d))
+    return (gv, ov, ga, oa, qv, qa, vb, ab, B)
+
+
+def test_joint_av_four_paths():
+    banner("joint A/V: v->v, a->a, v->a, a->v, streaming block 9 and all 10 blocks, bf16 H=32")
+    gv, ov, ga, oa, qv, qa, vb, ab, B = av_rings(WORKLOADS["av"].seed)
+    ov_g, oa_g = oracle_from_gpu(gv, 0.0), oracle_from_gpu(ga, 0.0)
+    for name, gring, oring, (qt, q), blen in [
+        ("v->v", gv, ov_g, qv, vb), ("a->a", ga, oa_g, qa, ab),
+        ("v->a", ga, oa_g, qv, vb), ("a->v", gv, ov_g, qa, ab)]:
+        # streaming: the last block's queries only
+        n = blen
+        out = gring.attention(qt[(B - 1) * n:].contiguous(), 0, B - 1, n, 0.0)
+        rows = np.unique(np.r_[0:n:max(1, n // 24), n - 1])
+        qlast = q[(B - 1) * n:]
+        ref, _ = oracle_rows(oring, qlast, rows, 0, B - 1, n, 0.0)
+        assert_attention_close(out, ref, "bf16", rows=rows)
+        # all blocks as queries (block-causal across them)
+        out_all = gring.attention(qt, 0, 0, blen, 0.0)
+        rows_all = np.unique(np.r_[0:B * blen:max(1, B * blen // 60), B * blen - 1])
+        ref_all, _ = oracle_rows(oring, q, rows_all, 0, 0, blen, 0.0)
+        assert_attention_close(out_all, ref_all, "bf16", rows=rows_all)
+        print(f"  {name}: ok", flush=True)
+
+
+def test_split_kv_matches_unsplit():
+    banner("attention: 25 audio queries over the 11520-slot video ring (split key range)")
+    gv, ov, ga, oa, qv, qa, vb, ab, B = av_rings(4)
+    qt, q = qa
+    qlast = qt[(B - 1) * ab:].contiguous()
+    assert gv.workspace_bytes(ab) > 0
+    lse1 = torch.empty((32, ab), dtype=torch.float32, device=DEV)
+    lse2 = torch.empty((32, ab), dtype=torch.float32, device=DEV)
+    split = gv.attention(qlast, 0, B - 1, ab, -0.3, lse=lse1)
+    nosplit = gv.attention(qlast, 0, B - 1, ab, -0.3, lse=lse2,
+                           workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    ref, ref_lse = ring_attention(oracle_from_gpu(gv, 0.0), q[(B - 1) * ab:], 0, B - 1, ab, -0.3)
+    assert_attention_close(split, ref, "bf16")
+    assert_attention_close(nosplit, ref, "bf16")
+    assert np.max(np.abs(to_np64(lse1) - ref_lse)) < 2e-2
+    assert np.max(np.abs(to_np64(lse2) - ref_lse)) < 2e-2
+
+
+# ------------------------------------------------------------------ masks
+def test_visibility_export_bit_exact():
+    banner("visibility predicate export vs oracle (empty slots, multi-block queries)")
+    rng = np.random.default_rng(3)
+    g, o = make_pair(300, 1, 64, "bf16", 0.0, first_slot=290)
+    for b, n in enumerate([40, 70, 33]):
+        write_both(g, o, rng, n, 10 * b, b * 2)  # blocks 0, 2, 4
+        g.advance(n)
+        o.advance(n)
+    for n_q, b0, bl in [(1, 0, 1), (90, 0, 20), (300, 1, 7), (64, 4, 64), (17, -3, 5)]:
+        m = g.visibility(n_q, b0, bl).cpu().numpy()
+        vis, earlier = visibility(o.slot_block, query_blocks(n_q, b0, bl))
+        want = np.where(earlier, 2, np.where(vis, 1, 0))
+        assert np.array_equal(m, want), (n_q, b0, bl)
+
+
+# ------------------------------------------------------------------ long run
+def test_longrun_scaled_schedule():
+    """The long-run schedule scaled down: 14 chunks over a 3-chunk ring, a
+    position reset every 5 chunks (delta rebases the oldest cached position
+    to 0), a bias ramp 0, -2, -4, -2, 0 over chunks 2..6, 2 denoising passes
+    per chunk.  Bookkeeping is compared every chunk, attention on every
+    chunk's last pass."""
+    banner("long run (scaled): 14 chunks, resets every 5, bias ramp, 2 passes")
+    from oracle.schedule import bias_at
+    rng = np.random.default_rng(WORKLOADS["longrun"].seed)
+    N, H, d, n = 300, 4, 128, 100
+    g, o = make_pair(N, H, d, "fp8", 10000.0)
+    pos = 0
+    worst = 0.0
+    for t in range(14):
+        if t > 0 and t % 5 == 0:
+            oldest = int(o.slot_pos[o.slot_block != -1].min())
+            g.rerotate(-oldest)
+            o.rerotate(-oldest)
+            pos -= oldest
+        beta = bias_at(t, n_ramps=1, first=2, spacing=1)
+        for _ in range(2):
+            write_both(g, o, rng, n, pos, t)
+            qt, q = inputs(rng, "fp8", (n, H, d))
+            out = g.attention(qt, pos, t, n, beta)
+        c = gpu_cache(g)
+        assert c["state"] == o.state()
+        assert np.array_equal(c["slot_block"], o.slot_block)
+        assert np.array_equal(c["slot_pos"][o.slot_block != -1], o.slot_pos[o.slot_block != -1])
+        ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, pos, t, n, beta)
+        err, _ = assert_attention_close(out, ref, "fp8")
+        ref_own, _ = ring_attention(o, q, pos, t, n, beta)
+        assert_attention_close(out, ref_own, "fp8")
+        worst = max(worst, err)
+        g.advance(n)
+        o.advance(n)
+        pos += n
+    print(f"  worst max-abs {worst:.3e}", flush=True)
