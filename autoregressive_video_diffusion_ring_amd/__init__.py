@@ -187,7 +187,7 @@ class Ring:
         return {RC_F32: torch.float32, RC_BF16: torch.bfloat16, RC_FP8_E4M3: torch.uint8}[self.kv]
 
     def k_raw(self):
-        return self._view(0, self._elem_dtype(), (self.H, self.N, self.d)).clone()
+        return self._view(0, self._elem_dtype(), (self.H, self.v_ld, self.d))[:, :self.N].clone()
 
     def v_raw(self):
         vt = self._view(1, self._elem_dtype(), (self.H, self.d, self.v_ld))

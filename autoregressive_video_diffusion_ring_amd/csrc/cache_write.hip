@@ -230,13 +230,12 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
         vs = row_scale<EPL>(xv);
       }
       if (valid) {
-        const size_t row = static_cast<size_t>(h) * N + s;
+        const size_t row = static_cast<size_t>(h) * a.r.v_ld + s;
         store_row<KV, EPL>(a.r.k, row * D + lane16 * EPL, xk, ks);
         if constexpr (KV == KV_FP8) {
           if (lane16 == 0) {
-            const size_t srow = static_cast<size_t>(h) * a.r.v_ld + s;
-            a.r.k_scale[srow] = ks;
-            a.r.v_scale[srow] = vs;
+            a.r.k_scale[row] = ks;
+            a.r.v_scale[row] = vs;
           }
         }
       }
@@ -296,9 +295,9 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
     const int h = row / r.N;
     const int s = row - h * r.N;
     if (r.slot_block[s] == -1) continue;  // the 16 lanes of a row branch together
-    const size_t off = static_cast<size_t>(row) * D + lane16 * EPL;
-    float x[EPL];
     const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
+    const size_t off = srow * D + lane16 * EPL;
+    float x[EPL];
     if constexpr (KV == KV_FP8) {
       const float sc = r.k_scale[srow];
       const uint8_t* p = static_cast<const uint8_t*>(r.k) + off;
@@ -373,7 +372,7 @@ hipError_t rerotate_impl(const RingView& r, int delta, hipStream_t s) {
 hipError_t launch_ring_clear(const RingView& r, hipStream_t s) {
   const size_t es = r.kv == KV_F32 ? 4 : (r.kv == KV_BF16 ? 2 : 1);
   hipError_t e;
-  if ((e = fill(r.k, static_cast<size_t>(r.H) * r.N * r.d * es, 0u, s)) != hipSuccess) return e;
+  if ((e = fill(r.k, static_cast<size_t>(r.H) * r.v_ld * r.d * es, 0u, s)) != hipSuccess) return e;
   if ((e = fill(r.v, static_cast<size_t>(r.H) * r.d * r.v_ld * es, 0u, s)) != hipSuccess) return e;
   if (r.kv == KV_FP8) {
     if ((e = fill(r.k_scale, static_cast<size_t>(r.H) * r.v_ld * 4, 0u, s)) != hipSuccess) return e;

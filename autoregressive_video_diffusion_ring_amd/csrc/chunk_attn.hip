@@ -134,19 +134,23 @@ __device__ __forceinline__ int k_perm(int mb, int m) {
   return 32 * ((m >> 2) & 1) + 16 * mb + 4 * (m >> 3) + (m & 3);
 }
 
-// XOR swizzles of 16-byte chunks against LDS bank conflicts.  K: the eight
-// lanes of a phase read slots {16mb + 0..3, 32 + 16mb + 0..3}.  V^T: they read
-// rows d .. d+7 at the same chunk.
+// XOR swizzles of 16-byte chunks against LDS bank conflicts, chosen by
+// measuring the conflict counter for each read pattern below: the K reads
+// take one chunk column of the slots k_perm(mb, 0..31), the V^T reads one
+// chunk column of 32 consecutive rows d.
 template <int KV, int D>
 __device__ __forceinline__ int k_swz(int slot) {
   constexpr int cpr = Tile<KV, D>::k_cpr;
-  const int s = (slot & 3) | ((slot >> 3) & 4);
-  return cpr >= 8 ? s : (s & (cpr - 1));
+  if constexpr (cpr == 4) return (slot ^ (slot >> 2)) & 3;   // 64-byte rows
+  else if constexpr (cpr == 8) return (slot >> 1) & 7;      // 128-byte rows
+  else return slot & 15;                                    // 256-byte rows
 }
 template <int KV, int D>
 __device__ __forceinline__ int v_swz(int d) {
   constexpr int cpr = Tile<KV, D>::v_cpr;
-  return cpr == 4 ? ((d >> 1) & 3) : (d & 7);
+  if constexpr (cpr == 4) return (d ^ (d >> 2)) & 3;
+  else if constexpr (cpr == 8) return (d >> 1) & 7;
+  else return d & 15;
 }
 template <int KV, int D>
 __device__ __forceinline__ int k_addr(int slot, int c) {
@@ -164,8 +168,9 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
 
 // Issue the direct-to-LDS loads of one tile for one key half.  Every wave of
 // the half moves whole 1 KB blocks (64 lanes x 16 bytes, contiguous in LDS);
-// each lane picks the global chunk that belongs at its LDS position.  Slots
-// past N read slot N-1 (finite data; such slots are masked by block -1).
+// each lane picks the global chunk that belongs at its LDS position.  K rows
+// are padded to v_ld slots per head, so a tile never reads past its head;
+// padding slots hold zeros and block -1.
 template <int KV, int D>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, int h, int tile, uint8_t* buf, int wq, int lane) {
   using T = Tile<KV, D>;
@@ -176,8 +181,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int h, int tile, ui
     const int p = blk * kWave + lane;  // LDS chunk index
     const int r = p / T::k_cpr, cp = p % T::k_cpr;
     const int cl = cp ^ k_swz<KV, D>(r);
-    const int key = min(key0 + r, a.N - 1);
-    dma16(a.k + (static_cast<size_t>(h) * a.N + key) * T::k_row + cl * 16, buf + T::k_off + blk * 1024);
+    dma16(a.k + (static_cast<size_t>(h) * a.v_ld + key0 + r) * T::k_row + cl * 16, buf + T::k_off + blk * 1024);
   }
 #pragma unroll
   for (int j = 0; j < T::v_instr; ++j) {

@@ -115,9 +115,9 @@ rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int3
   rc_status st = check_geometry(n_slots, n_heads, head_dim, kv_dtype);
   if (st != RC_OK) return st;
   const size_t es = elem_size(kv_dtype);
-  out[0] = static_cast<size_t>(n_heads) * n_slots * head_dim * es;
-  out[1] = static_cast<size_t>(n_heads) * head_dim * rc_ring_v_ld(n_slots) * es;
   const size_t ld = rc_ring_v_ld(n_slots);
+  out[0] = static_cast<size_t>(n_heads) * ld * head_dim * es;
+  out[1] = static_cast<size_t>(n_heads) * head_dim * ld * es;
   out[2] = out[3] = kv_dtype == RC_FP8_E4M3 ? static_cast<size_t>(n_heads) * ld * sizeof(float) : 0;
   out[4] = out[5] = ld * sizeof(int32_t);
   return ok();
@@ -187,6 +187,8 @@ rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32
                              void* workspace, size_t workspace_bytes, void* stream) {
   rc_status st = check_ring(r);
   if (st != RC_OK) return st;
+  if (!rc::attention_supported(r->kv_dtype, r->head_dim))
+    return fail(RC_ERR_UNSUPPORTED, "no attention kernel for float32 rings with head_dim %d", r->head_dim);
   if (!q || !out) return fail(RC_ERR_ARG, "q / out is NULL");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15u)
     return fail(RC_ERR_ARG, "q and out must be 16-byte aligned");

@@ -39,6 +39,8 @@ struct AttnCall {
   size_t workspace_bytes;
 };
 
+// Whether an attention kernel is built for this KV format and head size.
+bool attention_supported(int kv, int d);
 // Number of key splits the attention uses for n_q queries (1 = none).
 int attention_splits(const RingView& r, int n_q);
 size_t attention_workspace_bytes(const RingView& r, int n_q);

@@ -56,7 +56,7 @@ typedef enum {
  * pointers, then calls rc_ring_init, which sets the host state.
  *
  * Device layout (sizes from rc_ring_sizes):
- *   k          [H][N][d]        kv_dtype; row (h, s) is slot s of head h
+ *   k          [H][v_ld][d]     kv_dtype; row (h, s) is slot s of head h
  *   v          [H][d][v_ld]     kv_dtype, TRANSPOSED: v[h][j][s] is element
  *                               j of slot s; v_ld = rc_ring_v_ld(N) >= N
  *   k_scale    [H][v_ld] float  FP8 only: k = code * k_scale[h][s]
@@ -152,6 +152,8 @@ rc_status rc_cache_rerotate(rc_ring* ring, int32_t delta, void* stream);
  * slot_block[s] <= block(i).  logit = scale * (RoPE(q_i) . k_s) +
  * cache_bias * [slot_block[s] < block(i)].  A query that sees no slot gets
  * out = 0 and lse = -inf.  Requires n_q >= 1 and q_block_len >= 1.
+ * RC_ERR_UNSUPPORTED for an RC_F32 ring with head_dim 128 (float32 rings are
+ * a checking format; their attention kernel is built for head_dim 64 only).
  */
 rc_status rc_chunk_attention(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0,
                              int32_t q_block0, int32_t q_block_len, float cache_bias,

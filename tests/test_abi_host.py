@@ -66,9 +66,9 @@ def test_v_ld_and_sizes():
     assert [L.rc_ring_v_ld(n) for n in (1, 63, 64, 65, 5788, 11520)] == [64, 64, 64, 128, 5824, 11520]
     out = (ctypes.c_size_t * 6)()
     assert L.rc_ring_sizes(5788, 40, 128, RC_FP8_E4M3, out) == RC_OK
-    assert list(out) == [40 * 5788 * 128, 40 * 128 * 5824, 40 * 5824 * 4, 40 * 5824 * 4, 5824 * 4, 5824 * 4]
+    assert list(out) == [40 * 5824 * 128, 40 * 128 * 5824, 40 * 5824 * 4, 40 * 5824 * 4, 5824 * 4, 5824 * 4]
     assert L.rc_ring_sizes(96, 2, 64, RC_F32, out) == RC_OK
-    assert list(out) == [2 * 96 * 64 * 4, 2 * 64 * 128 * 4, 0, 0, 128 * 4, 128 * 4]
+    assert list(out) == [2 * 128 * 64 * 4, 2 * 64 * 128 * 4, 0, 0, 128 * 4, 128 * 4]
     assert L.rc_ring_sizes(96, 2, 96, RC_BF16, out) == RC_ERR_UNSUPPORTED
     assert L.rc_ring_sizes(0, 2, 64, RC_BF16, out) == RC_ERR_ARG
     assert L.rc_ring_sizes(10, 2, 64, 7, out) == RC_ERR_ARG
@@ -155,6 +155,9 @@ def test_attention_argument_checks():
     assert call(wsb=64) == RC_ERR_ARG
     r.head_dim = 96
     assert call() == RC_ERR_UNSUPPORTED
+    f = fake_ring(100, d=128, kv=RC_F32)
+    assert L.rc_chunk_attention(ctypes.byref(f), FAKE, 10, 0, 0, 10, 0.0, 0.0, FAKE, None, 0, 0,
+                                None) == RC_ERR_UNSUPPORTED
 
 
 def test_rerotate_needs_rope():

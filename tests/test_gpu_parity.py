@@ -231,7 +231,7 @@ def test_slot_permutation_invariance():
     a = to_np64(g.attention(qt, 500, 1, 100, -0.5))
     perm = torch.from_numpy(np.random.default_rng(2).permutation(640)).to(DEV)
     H, N, d = 4, 640, 128
-    kb = g.buffers[0].view(H, N, d)
+    kb = g.buffers[0].view(H, g.v_ld, d)[:, :N]
     kb.copy_(kb[:, perm].clone())
     vb = g.buffers[1].view(H, d, g.v_ld)
     vb[:, :, :N] = vb[:, :, :N][:, :, perm].clone()
