@@ -35,9 +35,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librc.so)")
 
 
+# The attention kernel handles no NaN inputs specially; without NaN
+# semantics its maxima compile to plain v_max3 instructions.
+EXTRA = {"chunk_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -108,24 +108,28 @@ struct Tile {
   static constexpr int k_off = 0;
   static constexpr int v_off = kKT * k_row;
   static constexpr int raw_off = v_off + D * v_row;  // k_scale[64], v_scale[64], block[64]
-  static constexpr int kfc_off = raw_off + 768;      // c * s_k
-  static constexpr int lv0_off = kfc_off + 256;      // log2 s_v
-  static constexpr int lv1_off = lv0_off + 256;      // log2 s_v + bias2
-  static constexpr int ivf_off = lv1_off + 256;      // 1 / s_v
-  static constexpr int bytes = ivf_off + 256;
+  static constexpr int bytes = raw_off + 768;
   static constexpr int k_instr = kKT * k_cpr / (kQSub * kWave);  // 16-byte DMA per wave
   static constexpr int v_instr = D * v_cpr / (kQSub * kWave);
   static_assert(kKT * k_cpr % (kQSub * kWave) == 0 && D * v_cpr % (kQSub * kWave) == 0, "tile split");
 };
 
+// Per-wave factors of one tile, one float per slot: A = c s_k, C = lb / A
+// (lb = log2 s_v, plus the bias when the whole tile takes it) and 1 / s_v.
+constexpr int kFacFloats = 3 * kKT;
+constexpr float kMinA = 0x1p-90f;  // floor of A, so that C stays finite
+
 template <int KV, int D>
 struct Stages {
   // Double buffering; each stage holds kps tiles per key half (two when they
-  // fit), so a tile's loads are issued two tile-computations ahead.
+  // fit).  The RoPE tables of the prologue live in the second stage buffer.
   static constexpr int rope_bytes = (64 + 8 * 64 + 16 * 64) * 8;
-  static constexpr int avail = 160 * 1024 - rope_bytes - 256;
-  static constexpr int kps = 2 * kHalves * 2 * Tile<KV, D>::bytes <= avail ? 2 : 1;
-  static_assert(2 * kHalves * kps * Tile<KV, D>::bytes <= avail, "LDS budget");
+  static constexpr int need(int kps) {
+    return 2 * kHalves * kps * Tile<KV, D>::bytes + kWaves * kps * kFacFloats * 4 + 256;
+  }
+  static constexpr int kps = need(2) <= 160 * 1024 ? 2 : 1;
+  static_assert(need(kps) <= 160 * 1024, "LDS budget");
+  static_assert(rope_bytes <= kHalves * kps * Tile<KV, D>::bytes, "RoPE tables fit in one stage");
 };
 
 // Slot (row of the K tile) that lane row m of M-block mb feeds into the QK
@@ -166,52 +170,67 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(lds_wave_base), 16, 0, 0);
 }
 
-// Issue the direct-to-LDS loads of one tile for one key half.  Every wave of
-// the half moves whole 1 KB blocks (64 lanes x 16 bytes, contiguous in LDS);
-// each lane picks the global chunk that belongs at its LDS position.  K rows
-// are padded to v_ld slots per head, so a tile never reads past its head;
-// padding slots hold zeros and block -1.
+// Direct-to-LDS loads of one tile for one key half.  Every wave of the half
+// moves whole 1 KB blocks (64 lanes x 16 bytes, contiguous in LDS); each lane
+// picks the global chunk that belongs at its LDS position.  The lane's byte
+// offsets do not depend on the tile, so they are computed once: a tile load
+// is a uniform base address plus these offsets.  K rows are padded to v_ld
+// slots per head, so a tile never reads past its head; padding slots hold
+// zeros and block -1.
 template <int KV, int D>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, int h, int tile, uint8_t* buf, int wq, int lane) {
+struct DmaPlan {
+  uint32_t k[Tile<KV, D>::k_instr];  // from the tile's first K row
+  uint32_t v[Tile<KV, D>::v_instr];  // from V^T[h][0][first slot of the tile]
+  const uint8_t* meta;               // k_scale / v_scale / slot_block piece of tile 0
+};
+// Per-slot metadata moves in one DMA instruction per wave, so every wave has
+// the same number of loads in flight: FP8 moves 48 chunks (k_scale, v_scale,
+// slot_block; 12 per wave), the other formats 16 (slot_block).
+template <int KV>
+struct MetaSplit {
+  static constexpr int per_wave = KV == KV_FP8 ? 12 : 4;
+  static constexpr int base_chunk = KV == KV_FP8 ? 0 : 32;
+};
+
+template <int KV, int D>
+__device__ __forceinline__ DmaPlan<KV, D> dma_plan(const AttnArgs& a, int h, int wq, int lane) {
   using T = Tile<KV, D>;
-  const int key0 = tile * kKT;
+  using M = MetaSplit<KV>;
+  DmaPlan<KV, D> pl;
 #pragma unroll
   for (int j = 0; j < T::k_instr; ++j) {
-    const int blk = wq * T::k_instr + j;
-    const int p = blk * kWave + lane;  // LDS chunk index
+    const int p = (wq * T::k_instr + j) * kWave + lane;  // LDS chunk index
     const int r = p / T::k_cpr, cp = p % T::k_cpr;
-    const int cl = cp ^ k_swz<KV, D>(r);
-    dma16(a.k + (static_cast<size_t>(h) * a.v_ld + key0 + r) * T::k_row + cl * 16, buf + T::k_off + blk * 1024);
+    pl.k[j] = static_cast<uint32_t>(r * T::k_row + ((cp ^ k_swz<KV, D>(r)) << 4));
   }
 #pragma unroll
   for (int j = 0; j < T::v_instr; ++j) {
-    const int blk = wq * T::v_instr + j;
-    const int p = blk * kWave + lane;
+    const int p = (wq * T::v_instr + j) * kWave + lane;
     const int d = p / T::v_cpr, cp = p % T::v_cpr;
-    const int cl = cp ^ v_swz<KV, D>(d);
-    dma16(a.v + ((static_cast<size_t>(h) * D + d) * a.v_ld + key0) * T::es + cl * 16,
-          buf + T::v_off + blk * 1024);
+    pl.v[j] = static_cast<uint32_t>(d * a.v_ld * T::es + ((cp ^ v_swz<KV, D>(d)) << 4));
   }
-  {
-    // per-slot metadata, one DMA instruction per wave so that every wave has
-    // the same number of loads in flight: FP8 moves 48 chunks (k_scale,
-    // v_scale, slot_block; 12 per wave), the other formats 16 (slot_block).
-    constexpr int per_wave = KV == KV_FP8 ? 12 : 4;
-    const int c = wq * per_wave + lane;  // chunk of the 768-byte raw area
-    const int base_chunk = KV == KV_FP8 ? 0 : 32;
-    if (lane < per_wave) {
-      const int cc = base_chunk + c, which = cc >> 4, j = (cc & 15) * 4;
-      const void* src = which == 0 ? static_cast<const void*>(a.k_scale + static_cast<size_t>(h) * a.v_ld + key0 + j)
-                        : which == 1 ? static_cast<const void*>(a.v_scale + static_cast<size_t>(h) * a.v_ld + key0 + j)
-                                     : static_cast<const void*>(a.slot_block + key0 + j);
-      dma16(src, buf + T::raw_off + (base_chunk + wq * per_wave) * 16);
-    }
-  }
+  const int cc = M::base_chunk + wq * M::per_wave + min(lane, M::per_wave - 1);
+  const int which = cc >> 4, j = (cc & 15) * 4;
+  const size_t hs = static_cast<size_t>(h) * a.v_ld + j;
+  pl.meta = which == 0 ? reinterpret_cast<const uint8_t*>(a.k_scale + hs)
+            : which == 1 ? reinterpret_cast<const uint8_t*>(a.v_scale + hs)
+                         : reinterpret_cast<const uint8_t*>(a.slot_block + j);
+  return pl;
 }
 
 template <int KV, int D>
-constexpr int dma_ops_per_tile() {
-  return Tile<KV, D>::k_instr + Tile<KV, D>::v_instr + 1;
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const DmaPlan<KV, D>& pl, int h, int tile,
+                                           uint8_t* buf, int wq, int lane) {
+  using T = Tile<KV, D>;
+  using M = MetaSplit<KV>;
+  const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + tile * kKT) * T::k_row;
+#pragma unroll
+  for (int j = 0; j < T::k_instr; ++j) dma16(kb + pl.k[j], buf + T::k_off + (wq * T::k_instr + j) * 1024);
+  const uint8_t* vb = a.v + (static_cast<size_t>(h) * D * a.v_ld + tile * kKT) * T::es;
+#pragma unroll
+  for (int j = 0; j < T::v_instr; ++j) dma16(vb + pl.v[j], buf + T::v_off + (wq * T::v_instr + j) * 1024);
+  if (lane < M::per_wave)
+    dma16(pl.meta + tile * (kKT * 4), buf + T::raw_off + (M::base_chunk + wq * M::per_wave) * 16);
 }
 
 // s_waitcnt vmcnt(N) as a real instruction (gfx9 encoding: vmcnt in bits
@@ -221,6 +240,9 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
@@ -261,6 +283,13 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
+// Four floats to four e4m3 codes written over `old`; both halves of the word
+// are replaced, so passing the word's previous value avoids clearing it.
+__device__ __forceinline__ int cvt_fp8x4_over(float a, float b, float c, float d, int old) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   using T = Tile<KV, D>;
@@ -271,12 +300,12 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   constexpr int kStageBytes = kHalves * KPS * T::bytes;
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) float2 rope_tab[64 + 8 * 64 + 16 * 64];
+  __shared__ __attribute__((aligned(16))) float fac[kWaves * KPS * kFacFloats];
   __shared__ float red[kWaves];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
   const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: kept in SGPRs
   const int kh = wave / kQSub;  // key half
   const int wq = wave % kQSub;  // query sub-tile (and wave index inside the half)
   const int n = lane & 31;
@@ -298,16 +327,13 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   auto tile_of = [&](int li) { return t_begin + 2 * li + kh; };
   auto has_tile = [&](int li) { return li < n_local && tile_of(li) < t_end; };
   auto tile_buf = [&](uint8_t* stage, int kk) { return stage + (kh * KPS + kk) * T::bytes; };
+  const DmaPlan<KV, D> plan = dma_plan<KV, D>(a, h, wq, lane);
   // Every step issues KPS tiles' loads for every wave (past the end a valid
   // tile is reloaded into a slot nobody reads), so wait counts are uniform.
-  auto issue_step = [&](uint8_t* stage, int st) {
-#pragma unroll
-    for (int kk = 0; kk < KPS; ++kk) {
-      const int li = st * KPS + kk;
-      load_tile<KV, D>(a, h, has_tile(li) ? tile_of(li) : t_begin, tile_buf(stage, kk), wq, lane);
-    }
+  auto issue = [&](uint8_t* stage, int st, int kk) {
+    const int li = st * KPS + kk;
+    issue_tile<KV, D>(a, plan, h, has_tile(li) ? tile_of(li) : t_begin, tile_buf(stage, kk), wq, lane);
   };
-
 
   // ---- queries of this lane
   const int q_base = qt * kQT;
@@ -351,12 +377,17 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   }
 
   // ---- start the first step's tiles
-  if (n_steps > 0) issue_step(st0, 0);
+  if (n_steps > 0) {
+#pragma unroll
+    for (int kk = 0; kk < KPS; ++kk) issue(st0, 0, kk);
+  }
   // ---- RoPE angle tables: e^{i pos theta_j} = e^{i P0 theta_j} e^{i 16 i1 theta_j} e^{i i0 theta_j}
   //      for pos = P0 + 16 i1 + i0 (angles formed in float64 before sincos).
-  float2* rE0 = rope_tab;                                                   // [64]
-  float2* rE1 = rE0 + 64;                                                  // [8][64]
-  float2* rE2 = rE1 + 8 * 64;                                              // [16][64]
+  //      They occupy the second stage buffer, which no load touches before
+  //      the first step's barrier.
+  float2* rE0 = reinterpret_cast<float2*>(st1);  // [64]
+  float2* rE1 = rE0 + 64;                         // [8][64]
+  float2* rE2 = rE1 + 8 * 64;                     // [16][64]
   const long long P0 = static_cast<long long>(a.q_pos0) + q_base;
   if (a.use_rope) {
 #pragma unroll
@@ -371,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         *dst = cs;
       }
     }
-    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    wait_lgkm0();
     bare_barrier();
   }
 
@@ -420,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
       for (int e = 0; e < D / 2; ++e) am = fmaxf(am, fabsf(x[e]));
       am = group_max<kWave>(am);
       if (lane == 0) red[wave] = am;
-      __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      wait_lgkm0();
       bare_barrier();
       am = red[0];
 #pragma unroll
@@ -453,31 +484,53 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = v16f{};
   float m_run = -INFINITY;  // stabiliser (log2 units)
+  float msub = 0.f;         // m_run, or 0 while it is -inf: logits are held as y - msub
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial sums of p
+  v8i pb = {};  // FP8 P^T operand, rewritten by every tile
+  float* wfac = fac + wave * (KPS * kFacFloats);
 
-  // Attention over one tile in LDS (skipped when no query of the wave sees it).
-  auto compute_tile = [&](const uint8_t* buf) {
-    const int kb = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512)[lane];
+  // Per-slot factors of one tile into this wave's own LDS area (lane = slot),
+  // and the wave-uniform tile class: vis (some query of the wave sees some
+  // slot) and fast (every slot visible to every query with one bias value).
+  auto factors = [&](const uint8_t* buf, float* wf, bool& vis, bool& fast) {
+    const int32_t kb = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512)[lane];
     const bool kval = kb != -1;
-    if (__ballot(kval && kb <= qb_hi) == 0ull) return;
+    vis = __ballot(kval && kb <= qb_hi) != 0ull;
     const bool all_vis = __ballot(!(kval && kb <= qb_lo)) == 0ull;
     const bool all_hist = __ballot(!(kval && kb < qb_lo)) == 0ull;
     const bool all_same = qb_lo == qb_hi && __ballot(!(kval && kb == qb_lo)) == 0ull;
-    // wave-uniform in an SGPR, so the branch below is a scalar branch
-    const int fast = __builtin_amdgcn_readfirstlane(all_vis && (all_hist || all_same || a.bias_log2 == 0.f));
+    fast = all_vis && (all_hist || all_same || a.bias_log2 == 0.f);
+    float A = c_mul, lv = 0.f, ivf = 1.f;
+    if constexpr (KV == KV_FP8) {
+      const float* raw = reinterpret_cast<const float*>(buf + T::raw_off);
+      const float vs = fmaxf(raw[64 + lane], kMinVScale);
+      A = fmaxf(c_mul * raw[lane], kMinA);
+      lv = __builtin_amdgcn_logf(vs);
+      ivf = __builtin_amdgcn_rcpf(vs);
+    }
+    const float lb = (fast && all_hist) ? lv + a.bias_log2 : lv;
+    wf[lane] = A;
+    wf[kKT + lane] = lb * __builtin_amdgcn_rcpf(A);
+    wf[2 * kKT + lane] = ivf;
+  };
 
-    // -- S^T = K Q^T: accumulator element i of lane group g is slot 32g + 16mb + i
-    v16f s[2];
+  // S'^T = K Q^T + C: accumulator element i of lane group g is slot
+  // 32g + 16mb + i, and starts at that slot's C so that A * S' = y.
+  auto qk = [&](const uint8_t* buf, const float* wf, v16f (&s)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = v16f{};
+      const float* cf = wf + kKT + 32 * g + 16 * mb;
+      const v4f c0 = *reinterpret_cast<const v4f*>(cf), c1 = *reinterpret_cast<const v4f*>(cf + 4);
+      const v4f c2 = *reinterpret_cast<const v4f*>(cf + 8), c3 = *reinterpret_cast<const v4f*>(cf + 12);
+      s[mb] = v16f{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                   c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
       const int slot = k_perm(mb, n);
       if constexpr (KV == KV_FP8) {
 #pragma unroll
         for (int ks = 0; ks < D / 64; ++ks) {
-          const int c0 = 4 * ks + 2 * g;
-          const v4i lo = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0));
-          const v4i hi = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0 + 1));
+          const int c0i = 4 * ks + 2 * g;
+          const v4i lo = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0i));
+          const v4i hi = *reinterpret_cast<const v4i*>(buf + k_addr<KV, D>(slot, c0i + 1));
           const v8i av = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf.q[ks], s[mb], 0, 0, 0, 0, 0, 0);
         }
@@ -496,74 +549,70 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         }
       }
     }
+  };
 
-    // -- y = c s_k S + log2 s_v (+ bias2), masked to -inf
-    const float* kfc = reinterpret_cast<const float*>(buf + T::kfc_off);
-    const float* lvsel = reinterpret_cast<const float*>(buf + (all_hist ? T::lv1_off : T::lv0_off));
-    const float* lv0 = reinterpret_cast<const float*>(buf + T::lv0_off);
-    const float* lv1 = reinterpret_cast<const float*>(buf + T::lv1_off);
-    const int32_t* kbs = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512);
-    float tmax = -INFINITY;
+  // Softmax update and O^T += V^T P^T for one tile.
+  auto smpv = [&](const uint8_t* buf, const float* wf, v16f (&s)[2], bool fast) {
+    // -- z = A S' - msub = y - msub, masked to -inf
+    const float negm = -msub;
     if (fast) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const int slot0 = 32 * g + 16 * mb + 4 * qq;
-          const v4f kf = *reinterpret_cast<const v4f*>(kfc + slot0);
-          const v4f lb = *reinterpret_cast<const v4f*>(lvsel + slot0);
-          s[mb][4 * qq + 0] = fmaf(s[mb][4 * qq + 0], kf.x, lb.x);
-          s[mb][4 * qq + 1] = fmaf(s[mb][4 * qq + 1], kf.y, lb.y);
-          s[mb][4 * qq + 2] = fmaf(s[mb][4 * qq + 2], kf.z, lb.z);
-          s[mb][4 * qq + 3] = fmaf(s[mb][4 * qq + 3], kf.w, lb.w);
+          const v4f af = *reinterpret_cast<const v4f*>(wf + 32 * g + 16 * mb + 4 * qq);
+          s[mb][4 * qq + 0] = fmaf(s[mb][4 * qq + 0], af.x, negm);
+          s[mb][4 * qq + 1] = fmaf(s[mb][4 * qq + 1], af.y, negm);
+          s[mb][4 * qq + 2] = fmaf(s[mb][4 * qq + 2], af.z, negm);
+          s[mb][4 * qq + 3] = fmaf(s[mb][4 * qq + 3], af.w, negm);
         }
     } else {
+      const int32_t* kbs = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int slot0 = 32 * g + 16 * mb + 4 * qq;
-          const v4f kf = *reinterpret_cast<const v4f*>(kfc + slot0);
-          const v4f l0 = *reinterpret_cast<const v4f*>(lv0 + slot0);
-          const v4f l1 = *reinterpret_cast<const v4f*>(lv1 + slot0);
+          const v4f af = *reinterpret_cast<const v4f*>(wf + slot0);
           const v4i kb4 = *reinterpret_cast<const v4i*>(kbs + slot0);
-          const float kfa[4] = {kf.x, kf.y, kf.z, kf.w};
-          const float l0a[4] = {l0.x, l0.y, l0.z, l0.w}, l1a[4] = {l1.x, l1.y, l1.z, l1.w};
+          const float afa[4] = {af.x, af.y, af.z, af.w};
           const int kba[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int cls = visibility_class(kba[r], my_qb);
-            const float y = fmaf(s[mb][4 * qq + r], kfa[r], cls == kVisBias ? l1a[r] : l0a[r]);
-            s[mb][4 * qq + r] = cls == kVisNone ? -INFINITY : y;
+            float z = fmaf(s[mb][4 * qq + r], afa[r], negm);
+            z = cls == kVisBias ? z + a.bias_log2 : z;
+            s[mb][4 * qq + r] = cls == kVisNone ? -INFINITY : z;
           }
         }
     }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    // -- tile maximum of this query (both lane groups)
+    float tmax;
+    {
       float m8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m8[e] = fmaxf(s[mb][2 * e], s[mb][2 * e + 1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m8[e] = fmaxf(m8[e], m8[e + 4]);
-      tmax = fmaxf(tmax, fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])));
-    }
-    {
+      for (int e = 0; e < 8; ++e) m8[e] = fmaxf(fmaxf(s[0][2 * e], s[0][2 * e + 1]), fmaxf(s[1][2 * e], s[1][2 * e + 1]));
+      tmax = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    if (__ballot(tmax > m_run + kTau) != 0ull) {
-      const float m_new = fmaxf(m_run, tmax);
+    // -- raise the stabiliser only when the tile maximum passes it by tau
+    if (__ballot(tmax + msub > m_run + kTau) != 0ull) {
+      const float m_new = fmaxf(m_run, tmax + msub);
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int r = 0; r < 4; ++r) l_part[r] *= alpha;
 #pragma unroll
       for (int b = 0; b < D / 32; ++b) o[b] *= alpha;
+      const float shift = m_new == -INFINITY ? 0.f : m_new - msub;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) s[mb] -= shift;
       m_run = m_new;
+      msub = m_new == -INFINITY ? 0.f : m_new;
     }
-    const float msub = m_run == -INFINITY ? 0.f : m_run;
 
-    // -- P~ = 2^(y - m); l += P~ / s_v
-    const float* ivfp = reinterpret_cast<const float*>(buf + T::ivf_off);
+    // -- P~ = 2^z; l += P~ / s_v
+    const float* ivfp = wf + 2 * kKT;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -572,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         const float iva[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[mb][4 * qq + r] - msub);
+          const float p = __builtin_amdgcn_exp2f(s[mb][4 * qq + r]);
           s[mb][4 * qq + r] = p;
           l_part[r] = fmaf(p, iva[r], l_part[r]);
         }
@@ -581,13 +630,12 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
 
     // -- O^T += V^T P^T (reduction index: slot 32g + j of the tile)
     if constexpr (KV == KV_FP8) {
-      v8i pb;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
-          pb[4 * mb + qq] = static_cast<int>(
-              cvt_fp8x4(s[mb][4 * qq], s[mb][4 * qq + 1], s[mb][4 * qq + 2], s[mb][4 * qq + 3]));
+          pb[4 * mb + qq] = cvt_fp8x4_over(s[mb][4 * qq], s[mb][4 * qq + 1], s[mb][4 * qq + 2],
+                                           s[mb][4 * qq + 3], pb[4 * mb + qq]);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int d = 32 * db + n;
@@ -627,40 +675,38 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   };
 
   // One pipeline step: the KPS tiles of stage `cur` are computed while the
-  // next step's tiles land in `nxt`.
+  // next step's tiles are loaded into `nxt`.  The loads are issued between
+  // the tiles' matrix work rather than all at once, so that no wave stalls
+  // on a full load queue.
   auto step = [&](uint8_t* cur, uint8_t* nxt, int st) {
-    wait_vm<0>();    // this step's loads (issued one step ago) have landed
-    bare_barrier();  // B1: visible to all waves; every wave is done with `nxt`
-    if (st + 1 < n_steps) issue_step(nxt, st + 1);
-    if (wq == 0) {
-      // per-slot factors of each tile (one lane per slot)
+    wait_vm<0>();    // this wave's loads of this step have landed
+    bare_barrier();  // every wave's: visible to all; every wave is done with `nxt`
+    const bool more = st + 1 < n_steps;
+    if (!wave_active) {
+      if (more) {
 #pragma unroll
-      for (int kk = 0; kk < KPS; ++kk) {
-        if (!has_tile(st * KPS + kk)) continue;
-        uint8_t* buf = tile_buf(cur, kk);
-        const float* raw = reinterpret_cast<const float*>(buf + T::raw_off);
-        float kfc = c_mul, lv = 0.f, ivf = 1.f;
-        if constexpr (KV == KV_FP8) {
-          const float vs = fmaxf(raw[64 + lane], kMinVScale);
-          kfc = c_mul * raw[lane];
-          lv = __builtin_amdgcn_logf(vs);
-          ivf = __builtin_amdgcn_rcpf(vs);
-        }
-        reinterpret_cast<float*>(buf + T::kfc_off)[lane] = kfc;
-        reinterpret_cast<float*>(buf + T::lv0_off)[lane] = lv;
-        reinterpret_cast<float*>(buf + T::lv1_off)[lane] = lv + a.bias_log2;
-        reinterpret_cast<float*>(buf + T::ivf_off)[lane] = ivf;
+        for (int kk = 0; kk < KPS; ++kk) issue(nxt, st + 1, kk);
       }
+      return;
     }
-    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-    bare_barrier();  // B2: per-slot factors visible
-    // Already satisfied (this step's loads were waited for before B1); tells
-    // the compiler's wait analysis that only the next step's loads are in flight.
-    wait_vm<KPS * dma_ops_per_tile<KV, D>()>();
-    if (!wave_active) return;
+    bool vis[KPS], fast[KPS];
 #pragma unroll
-    for (int kk = 0; kk < KPS; ++kk)
-      if (has_tile(st * KPS + kk)) compute_tile(tile_buf(cur, kk));
+    for (int kk = 0; kk < KPS; ++kk) {
+      vis[kk] = false;
+      fast[kk] = false;
+      if (has_tile(st * KPS + kk)) factors(tile_buf(cur, kk), wfac + kk * kFacFloats, vis[kk], fast[kk]);
+    }
+    v16f s[KPS][2];
+#pragma unroll
+    for (int kk = 0; kk < KPS; ++kk) {
+      if (vis[kk]) qk(tile_buf(cur, kk), wfac + kk * kFacFloats, s[kk]);
+      if (kk == 0 && more) issue(nxt, st + 1, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPS; ++kk) {
+      if (vis[kk]) smpv(tile_buf(cur, kk), wfac + kk * kFacFloats, s[kk], fast[kk]);
+      if (kk + 1 < KPS && more) issue(nxt, st + 1, kk + 1);
+    }
   };
   for (int st = 0; st < n_steps; st += 2) {
     step(st0, st1, st);
