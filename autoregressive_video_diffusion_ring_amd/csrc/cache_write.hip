@@ -4,19 +4,21 @@
 // to K and FP8 quantisation to both at write time, and the re-rotation moves
 // every cached key to new positions by a delta rotation (Runway Characters,
 // abstract).  Both are HBM-bound: each byte of input is read once and each
-// byte of the cache written once.
+// byte of the cache written once, so both are organised to keep many loads
+// in flight: every thread issues all of its loads before any arithmetic.
 //
 // Write layout: the written range [head, head + n) mod N is cut into at most
-// two linear slot ranges, and each range into 64-slot chunks aligned to
-// multiples of 64.  One workgroup handles one chunk for a group of heads:
-//  * cos/sin of every (slot, pair) of the chunk go to LDS once and are reused
-//    for every head of the group;
-//  * a K row (one token of one head, d elements) is handled by 16 lanes, so a
-//    pass of 256 threads covers 16 slots; each lane stores d/16 contiguous
-//    elements and the 16 lanes a whole contiguous cache row;
+// two linear slot ranges, and each range into 32-slot chunks aligned to
+// multiples of 32.  One workgroup handles one chunk for kWHeads heads:
+//  * cos/sin of every (slot, pair) of the chunk go to LDS once, built from
+//    one float64-reduced angle per frequency at the chunk's first position
+//    times small-angle factors, and are reused for every head;
+//  * a row (one token of one head, d elements) is handled by 16 lanes with
+//    d/16 contiguous elements each, so a row's loads and stores are whole
+//    contiguous cache rows;
 //  * V is quantised the same way, transposed through LDS and stored to the
-//    [H][d][v_ld] layout as 16-byte pieces of each row (64-slot chunks start
-//    on a multiple of 64 and v_ld is a multiple of 64, so pieces are aligned).
+//    [H][d][v_ld] layout as 16-byte pieces (chunks start on a multiple of 32
+//    and v_ld is a multiple of 64, so pieces are aligned).
 #include <algorithm>
 #include <cmath>
 
@@ -27,9 +29,11 @@ namespace rc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;
+constexpr int kWChunk = 32;                  // slots per write workgroup
+constexpr int kWHeads = 2;                   // heads per write workgroup
 constexpr int kLanesPerRow = 16;
-constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+constexpr int kRowGroups = kThreads / kLanesPerRow;
+constexpr int kRowsPerThread = kWChunk * kWHeads / kRowGroups;
 
 template <int KV>
 struct Store;
@@ -52,42 +56,48 @@ struct WriteArgs {
   const void* v_new;
   int n_new, head, pos0, block_id;
   int lo_a, hi_a, lo_b, hi_b, chunks_a;
-  int heads_per_group;
+  int chunks, items;  // chunks per head group; chunks x head groups
   int use_rope;
   RopeTable rope;
 };
 
-// Loads EPL input elements of one (token, head) row, as float.
+// Raw input words of one row piece: EPL elements, bf16 pairs or floats.
 template <int KV, int EPL>
-__device__ __forceinline__ void load_row(const void* base, size_t elem_off, float* x) {
-  if constexpr (KV == KV_F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+struct Raw {
+  static constexpr int words = KV == KV_F32 ? EPL : EPL / 2;
+  uint32_t w[words];
+};
+
+template <int KV, int EPL>
+__device__ __forceinline__ void load_raw(const void* base, size_t elem_off, Raw<KV, EPL>& r) {
+  constexpr int W = Raw<KV, EPL>::words;
+  const uint8_t* p = static_cast<const uint8_t*>(base) + elem_off * (KV == KV_F32 ? 4 : 2);
+  if constexpr (W % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < EPL / 4; ++i) {
-      float4 t = p[i];
-      x[4 * i] = t.x;
-      x[4 * i + 1] = t.y;
-      x[4 * i + 2] = t.z;
-      x[4 * i + 3] = t.w;
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[i];
+      r.w[4 * i] = t.x;
+      r.w[4 * i + 1] = t.y;
+      r.w[4 * i + 2] = t.z;
+      r.w[4 * i + 3] = t.w;
     }
   } else {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + elem_off;
-    if constexpr (EPL == 8) {
-      uint4 t = *reinterpret_cast<const uint4*>(p);
-      uint32_t w[4] = {t.x, t.y, t.z, t.w};
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = t.x;
+    r.w[1] = t.y;
+  }
+}
+
+template <int KV, int EPL>
+__device__ __forceinline__ void unpack(const Raw<KV, EPL>& r, float* x) {
+  if constexpr (KV == KV_F32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-      uint2 t = *reinterpret_cast<const uint2*>(p);
-      uint32_t w[2] = {t.x, t.y};
+    for (int i = 0; i < EPL; ++i) x[i] = __uint_as_float(r.w[i]);
+  } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
+    for (int i = 0; i < EPL / 2; ++i) {
+      x[2 * i] = __uint_as_float(r.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
     }
   }
 }
@@ -96,44 +106,65 @@ __device__ __forceinline__ void load_row(const void* base, size_t elem_off, floa
 // that follows (round to nearest even) yields the correctly rounded code of
 // the exact quotient.  A plain float32 quotient can land exactly on a
 // midpoint between two FP8 codes when the exact quotient lies just beside it
-// (common: x and the absmax carry 8 significant bits, so 448 x / absmax is
-// often a short fraction, while scale = absmax / 448 is rounded), and the
-// conversion's tie-break would then round the wrong way.  Round-to-odd keeps
-// the "inexact" information in the last bit (float32 has 20 more bits than
-// e4m3), the classical remedy for double rounding.  A zero scale gives 0.
-__device__ __forceinline__ float qdiv(float x, float scale) {
-  if (!(scale > 0.f)) return 0.f;
-  const float q = x / scale;             // correctly rounded
-  const float r = fmaf(-q, scale, x);    // exact remainder x - q * scale
-  if (r == 0.f || q == 0.f) return q;
-  uint32_t u = __float_as_uint(q);
-  if ((r > 0.f) != (q > 0.f)) u -= 1;    // exact quotient is nearer zero: truncate
-  return __uint_as_float(u | 1u);        // inexact: force the last bit to 1
+// (common for unrotated input: x and the absmax carry 8 significant bits, so
+// 448 x / absmax is often a short fraction, while scale = absmax / 448 is
+// rounded), and the conversion's tie-break would then round the wrong way.
+// Round-to-odd keeps the "inexact" information in the last bit (float32 has
+// 20 more bits than e4m3), the classical remedy for double rounding.
+//
+// The quotient comes from rcp ~ 1/scale and one Newton step, which leaves it
+// within one ulp of x / scale; the remainder x - q scale is then exact (one
+// FMA), and its sign gives the truncation and the sticky bit.  Callers pass
+// rcp = 0 for an all-zero row (scale 0), which yields 0.
+__device__ __forceinline__ float qdiv_rto(float x, float scale, float rcp) {
+  const float q0 = x * rcp;
+  const float e0 = fmaf(-q0, scale, x);
+  const float q = fmaf(e0, rcp, q0);
+  const float e = fmaf(-q, scale, x);
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t t = (u - ((__float_as_uint(e) ^ u) >> 31)) | 1u;  // toward zero if e opposes q
+  return e == 0.f ? q : __uint_as_float(t);
 }
 
-// Stores EPL values of a K row: FP8 codes (given the row's scale), bf16 or
-// float32.
-template <int KV, int EPL>
-__device__ __forceinline__ void store_row(void* base, size_t elem_off, const float* x, float sc) {
+// Reciprocal of a row scale for the quotients above (0 for a zero row).
+__device__ __forceinline__ float scale_rcp(float scale) {
+  return scale > 0.f ? __builtin_amdgcn_rcpf(scale) : 0.f;
+}
+
+// Encodes EPL values as FP8 codes of the given scale.  EXACT: correctly
+// rounded codes of the exact quotients (needed where inputs are short
+// binary fractions, so that ties are common); otherwise the float32 product
+// x * (1/scale), within a few float32 ulps of the quotient, is converted
+// directly (used for keys that were just rotated in float32, whose values
+// already carry float32 rounding and essentially never sit on a tie).
+template <int EPL, bool EXACT>
+__device__ __forceinline__ void encode_fp8(const float* x, float sc, float rcp, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < EPL / 4; ++i) {
+    float q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = EXACT ? qdiv_rto(x[4 * i + k], sc, rcp) : x[4 * i + k] * rcp;
+    w[i] = cvt_fp8x4(q[0], q[1], q[2], q[3]);
+  }
+}
+
+// Stores EPL values of a K row piece: FP8 codes, bf16 or float32.
+template <int KV, int EPL, bool EXACT>
+__device__ __forceinline__ void store_row(void* base, size_t elem_off, const float* x, float sc, float rcp) {
   if constexpr (KV == KV_FP8) {
+    uint32_t w[EPL / 4];
+    encode_fp8<EPL, EXACT>(x, sc, rcp, w);
     uint8_t* p = static_cast<uint8_t*>(base) + elem_off;
-    if constexpr (EPL == 8) {
-      uint2 w;
-      w.x = cvt_fp8x4(qdiv(x[0], sc), qdiv(x[1], sc), qdiv(x[2], sc), qdiv(x[3], sc));
-      w.y = cvt_fp8x4(qdiv(x[4], sc), qdiv(x[5], sc), qdiv(x[6], sc), qdiv(x[7], sc));
-      *reinterpret_cast<uint2*>(p) = w;
-    } else {
-      *reinterpret_cast<uint32_t*>(p) = cvt_fp8x4(qdiv(x[0], sc), qdiv(x[1], sc), qdiv(x[2], sc), qdiv(x[3], sc));
-    }
+    if constexpr (EPL == 16) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else if constexpr (EPL == 8) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint32_t*>(p) = w[0];
   } else if constexpr (KV == KV_BF16) {
     uint16_t* p = static_cast<uint16_t*>(base) + elem_off;
     if constexpr (EPL == 8) {
-      uint4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                 pack_bf16x2(x[6], x[7])};
-      *reinterpret_cast<uint4*>(p) = w;
+      *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
     } else {
-      uint2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-      *reinterpret_cast<uint2*>(p) = w;
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
     }
   } else {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + elem_off);
@@ -142,14 +173,14 @@ __device__ __forceinline__ void store_row(void* base, size_t elem_off, const flo
   }
 }
 
-// Row absmax over the 16 lanes of a row -> scale = max|x| / 448 in float32
+// Absmax over the LANES lanes of a row -> scale = max|x| / 448 in float32
 // (IEEE division); a zero row gives 0.
-template <int EPL>
+template <int LANES, int EPL>
 __device__ __forceinline__ float row_scale(const float* x) {
   float a = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
-  a = group_max<kLanesPerRow>(a);
+  a = group_max<LANES>(a);
   return a / 448.0f;
 }
 
@@ -157,176 +188,249 @@ template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   constexpr int EPL = D / kLanesPerRow;
   constexpr int ES = Store<KV>::bytes;
-  __shared__ float2 cs[kChunk][D / 2];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[D * kChunk * ES];
+  constexpr int RJ = D / 2;  // RoPE pairs
+  __shared__ float2 cs[kWChunk][RJ];
+  __shared__ float2 e0[RJ], e1[kWChunk / 8][RJ], e2[8][RJ];
+  // V^T rows of the chunk, padded by 4 bytes against bank conflicts of the
+  // transposing byte writes (rows are read back as 4-byte words)
+  constexpr int RS = kWChunk * ES + 4;
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kWHeads * D * RS];
 
   const int tid = threadIdx.x;
-  const int N = a.r.N;
-  const int c = blockIdx.x;
+  const int N = a.r.N, H = a.r.H;
+  // Workgroups are dealt to the 8 XCDs in turn; give each XCD a contiguous
+  // range of work items, so that the neighbouring chunks whose V^T pieces
+  // share 128-byte lines are written through the same L2.
+  const int per_xcd = gridDim.x / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= a.items) return;
+  const int c = item % a.chunks;
+  const int group = item / a.chunks;
   int base, lo, hi;
   if (c < a.chunks_a) {
-    base = (a.lo_a / kChunk + c) * kChunk;
+    base = (a.lo_a / kWChunk + c) * kWChunk;
     lo = max(base, a.lo_a);
-    hi = min(base + kChunk, a.hi_a);
+    hi = min(base + kWChunk, a.hi_a);
   } else {
-    base = (a.lo_b / kChunk + (c - a.chunks_a)) * kChunk;
+    base = (a.lo_b / kWChunk + (c - a.chunks_a)) * kWChunk;
     lo = max(base, a.lo_b);
-    hi = min(base + kChunk, a.hi_b);
+    hi = min(base + kWChunk, a.hi_b);
   }
+  // token index of slot s (slots of one chunk have consecutive tokens)
   auto token_of = [&](int s) {
     int t = s - a.head;
     return t < 0 ? t + N : t;
   };
+  const int h0 = group * kWHeads;
+  const int piece = tid % kLanesPerRow;
+  const int rg = tid / kLanesPerRow;
 
-  if (a.use_rope) {
-    for (int e = tid; e < kChunk * (D / 2); e += kThreads) {
-      int r = e / (D / 2), j = e - r * (D / 2);
-      int s = base + r;
-      float cc = 1.f, ss = 0.f;
-      if (s >= lo && s < hi) rope_cs(a.rope, j, static_cast<long long>(a.pos0) + token_of(s), &cc, &ss);
-      cs[r][j] = make_float2(cc, ss);
+  // ---- all input loads first
+  Raw<KV, EPL> rk[kRowsPerThread], rv[kRowsPerThread];
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int row = rg + i * kRowGroups;
+    const int sl = row % kWChunk, hh = row / kWChunk;
+    const int s = base + sl, h = h0 + hh;
+#pragma unroll
+    for (int w = 0; w < Raw<KV, EPL>::words; ++w) rk[i].w[w] = rv[i].w[w] = 0u;
+    if (s >= lo && s < hi && h < H) {
+      const size_t off = (static_cast<size_t>(token_of(s)) * H + h) * D + piece * EPL;
+      load_raw<KV, EPL>(a.k_new, off, rk[i]);
+      load_raw<KV, EPL>(a.v_new, off, rv[i]);
     }
-    __syncthreads();
   }
 
-  if (blockIdx.y == 0 && tid < kChunk) {
-    int s = base + tid;
+  // ---- slot metadata (first head group only)
+  if (group == 0 && tid < kWChunk) {
+    const int s = base + tid;
     if (s >= lo && s < hi) {
       a.r.slot_pos[s] = a.pos0 + token_of(s);
       a.r.slot_block[s] = a.block_id;
     }
   }
 
-  const int lane16 = tid % kLanesPerRow;
-  const int h0 = blockIdx.y * a.heads_per_group;
-  const int h1 = min(h0 + a.heads_per_group, a.r.H);
-  const int H = a.r.H;
-  for (int h = h0; h < h1; ++h) {
-#pragma unroll
-    for (int p = 0; p < kChunk / kRowsPerPass; ++p) {
-      const int r = p * kRowsPerPass + tid / kLanesPerRow;
-      const int s = base + r;
-      const bool valid = s >= lo && s < hi;
-      float xk[EPL], xv[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) xk[e] = xv[e] = 0.f;
-      if (valid) {
-        const size_t off = (static_cast<size_t>(token_of(s)) * H + h) * D + lane16 * EPL;
-        load_row<KV, EPL>(a.k_new, off, xk);
-        load_row<KV, EPL>(a.v_new, off, xv);
-      }
-      if (a.use_rope) {
-#pragma unroll
-        for (int e = 0; e < EPL / 2; ++e) {
-          float2 t = cs[r][lane16 * (EPL / 2) + e];
-          float x0 = xk[2 * e], x1 = xk[2 * e + 1];
-          xk[2 * e] = x0 * t.x - x1 * t.y;
-          xk[2 * e + 1] = x0 * t.y + x1 * t.x;
-        }
-      }
-      float ks = 0.f, vs = 0.f;
-      if constexpr (KV == KV_FP8) {
-        ks = row_scale<EPL>(xk);
-        vs = row_scale<EPL>(xv);
-      }
-      if (valid) {
-        const size_t row = static_cast<size_t>(h) * a.r.v_ld + s;
-        store_row<KV, EPL>(a.r.k, row * D + lane16 * EPL, xk, ks);
-        if constexpr (KV == KV_FP8) {
-          if (lane16 == 0) {
-            a.r.k_scale[row] = ks;
-            a.r.v_scale[row] = vs;
-          }
-        }
-      }
-      // V to LDS, transposed [D][kChunk]
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int j = lane16 * EPL + e;
-        if constexpr (KV == KV_FP8) {
-          if (e % 2 == 0) {
-            const uint32_t w =
-                static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qdiv(xv[e], vs), qdiv(xv[e + 1], vs), 0, false));
-            vt[j * kChunk + r] = static_cast<uint8_t>(w & 0xFF);
-            vt[(j + 1) * kChunk + r] = static_cast<uint8_t>((w >> 8) & 0xFF);
-          }
-        } else if constexpr (KV == KV_BF16) {
-          reinterpret_cast<uint16_t*>(vt)[j * kChunk + r] = f32_to_bf16(xv[e]);
-        } else {
-          reinterpret_cast<float*>(vt)[j * kChunk + r] = xv[e];
-        }
-      }
+  // ---- RoPE table of the chunk, while the loads are in flight:
+  //      e^{i (P + t) theta_j} = e^{i P theta_j} e^{i 8 (t / 8) theta_j} e^{i (t % 8) theta_j}
+  //      with P the position of the chunk's first slot (the first factor's
+  //      angle reduced in float64).
+  if (a.use_rope) {
+    const long long P = static_cast<long long>(a.pos0) + token_of(lo) - (lo - base);
+    constexpr int kE = RJ * (1 + kWChunk / 8 + 8);
+    for (int e = tid; e < kE; e += kThreads) {
+      const int row = e / RJ, j = e % RJ;
+      const long long pos = row == 0 ? P : (row <= kWChunk / 8 ? 8LL * (row - 1) : static_cast<long long>(row - 1 - kWChunk / 8));
+      float2 v;
+      rope_cs(a.rope, j, pos, &v.x, &v.y);
+      if (row == 0) e0[j] = v;
+      else if (row <= kWChunk / 8) e1[row - 1][j] = v;
+      else e2[row - 1 - kWChunk / 8][j] = v;
     }
     __syncthreads();
-    // transposed V rows -> global, 16-byte pieces
-    constexpr int kSlotsPerPiece = 16 / ES;
-    constexpr int kPiecesPerRow = kChunk / kSlotsPerPiece;
-    for (int u = tid; u < D * kPiecesPerRow; u += kThreads) {
-      const int j = u / kPiecesPerRow, w = u - j * kPiecesPerRow;
-      const int s0 = base + w * kSlotsPerPiece;
-      const uint8_t* src = vt + (j * kChunk + w * kSlotsPerPiece) * ES;
-      uint8_t* dst = static_cast<uint8_t*>(a.r.v) +
-                     ((static_cast<size_t>(h) * D + j) * a.r.v_ld + s0) * ES;
-      if (s0 >= lo && s0 + kSlotsPerPiece <= hi) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-      } else {
-        for (int q = 0; q < kSlotsPerPiece; ++q) {
-          if (s0 + q >= lo && s0 + q < hi) {
-#pragma unroll
-            for (int b = 0; b < ES; ++b) dst[q * ES + b] = src[q * ES + b];
-          }
-        }
-      }
+    for (int e = tid; e < kWChunk * RJ; e += kThreads) {
+      const int t = e / RJ, j = e % RJ;
+      const float2 p = e0[j], q = e1[t / 8][j], r = e2[t % 8][j];
+      const float2 pq = make_float2(p.x * q.x - p.y * q.y, p.x * q.y + p.y * q.x);
+      cs[t][j] = make_float2(pq.x * r.x - pq.y * r.y, pq.x * r.y + pq.y * r.x);
     }
     __syncthreads();
   }
+
+  // ---- rows: rotate, quantise, store K; quantise V into LDS (transposed)
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int row = rg + i * kRowGroups;
+    const int sl = row % kWChunk, hh = row / kWChunk;
+    const int s = base + sl, h = h0 + hh;
+    const bool valid = s >= lo && s < hi && h < H;
+    float xk[EPL], xv[EPL];
+    unpack<KV, EPL>(rk[i], xk);
+    unpack<KV, EPL>(rv[i], xv);
+    if (a.use_rope) {
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) {
+        const float2 t = cs[sl][piece * (EPL / 2) + e];
+        const float x0 = xk[2 * e], x1 = xk[2 * e + 1];
+        xk[2 * e] = x0 * t.x - x1 * t.y;
+        xk[2 * e + 1] = x0 * t.y + x1 * t.x;
+      }
+    }
+    float ks = 0.f, vs = 0.f, krc = 0.f, vrc = 0.f;
+    if constexpr (KV == KV_FP8) {
+      ks = row_scale<kLanesPerRow, EPL>(xk);
+      vs = row_scale<kLanesPerRow, EPL>(xv);
+      krc = scale_rcp(ks);
+      vrc = scale_rcp(vs);
+    }
+    if (valid) {
+      const size_t srow = static_cast<size_t>(h) * a.r.v_ld + s;
+      // rotated keys: direct product; unrotated keys: exact quotient
+      if (a.use_rope) store_row<KV, EPL, false>(a.r.k, srow * D + piece * EPL, xk, ks, krc);
+      else store_row<KV, EPL, true>(a.r.k, srow * D + piece * EPL, xk, ks, krc);
+      if constexpr (KV == KV_FP8) {
+        if (piece == 0) {
+          a.r.k_scale[srow] = ks;
+          a.r.v_scale[srow] = vs;
+        }
+      }
+    }
+    // V^T in LDS: row (hh, j) at (hh * D + j) * RS, slot sl at sl * ES
+    uint8_t* vcol = vt + static_cast<size_t>(hh) * D * RS + (piece * EPL) * RS + sl * ES;
+    if constexpr (KV == KV_FP8) {
+      uint32_t w[EPL / 4];
+      encode_fp8<EPL, true>(xv, vs, vrc, w);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vcol[e * RS] = static_cast<uint8_t>(w[e / 4] >> (8 * (e % 4)));
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) *reinterpret_cast<uint16_t*>(vcol + e * RS) = f32_to_bf16(xv[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) *reinterpret_cast<float*>(vcol + e * RS) = xv[e];
+    }
+  }
+  __syncthreads();
+
+  // ---- V^T rows -> global, 16-byte pieces
+  constexpr int kSlotsPerPiece = 16 / ES;
+  constexpr int kPiecesPerRow = kWChunk / kSlotsPerPiece;
+  for (int u = tid; u < kWHeads * D * kPiecesPerRow; u += kThreads) {
+    const int hh = u / (D * kPiecesPerRow);
+    const int rem = u - hh * (D * kPiecesPerRow);
+    const int j = rem / kPiecesPerRow, w = rem - j * kPiecesPerRow;
+    const int h = h0 + hh;
+    if (h >= H) continue;
+    const int s0 = base + w * kSlotsPerPiece;
+    const uint8_t* src = vt + (static_cast<size_t>(hh) * D + j) * RS + w * 16;
+    uint8_t* dst = static_cast<uint8_t*>(a.r.v) + ((static_cast<size_t>(h) * D + j) * a.r.v_ld + s0) * ES;
+    if (s0 >= lo && s0 + kSlotsPerPiece <= hi) {
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(s32[0], s32[1], s32[2], s32[3]);
+    } else {
+      for (int q = 0; q < kSlotsPerPiece; ++q) {
+        if (s0 + q >= lo && s0 + q < hi) {
+#pragma unroll
+          for (int b = 0; b < ES; ++b) dst[q * ES + b] = src[q * ES + b];
+        }
+      }
+    }
+  }
 }
+
+// Delta re-rotation of every occupied row.  A row of K (d elements) is
+// handled by LPR lanes with 16 bytes each; a thread takes kRotRows rows whose
+// loads are all issued before any arithmetic.
+constexpr int kRotRows = 4;
 
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delta, RopeTable rope) {
-  constexpr int EPL = D / kLanesPerRow;
-  const int lane16 = threadIdx.x % kLanesPerRow;
-  float cc[EPL / 2], ss[EPL / 2];
+  constexpr int ES = Store<KV>::bytes;
+  constexpr int EPT = 16 / ES;          // elements per thread
+  constexpr int LPR = D / EPT;          // lanes per row
+  constexpr int RPB = kThreads / LPR;   // rows per block pass
+  const int lane = threadIdx.x % LPR;
+  float cc[EPT / 2], ss[EPT / 2];
 #pragma unroll
-  for (int e = 0; e < EPL / 2; ++e) rope_cs(rope, lane16 * (EPL / 2) + e, delta, &cc[e], &ss[e]);
+  for (int e = 0; e < EPT / 2; ++e) rope_cs(rope, lane * (EPT / 2) + e, delta, &cc[e], &ss[e]);
   const int rows = r.H * r.N;
-  for (int row = blockIdx.x * kRowsPerPass + threadIdx.x / kLanesPerRow; row < rows;
-       row += gridDim.x * kRowsPerPass) {
-    const int h = row / r.N;
-    const int s = row - h * r.N;
-    if (r.slot_block[s] == -1) continue;  // the 16 lanes of a row branch together
-    const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
-    const size_t off = srow * D + lane16 * EPL;
-    float x[EPL];
-    if constexpr (KV == KV_FP8) {
-      const float sc = r.k_scale[srow];
-      const uint8_t* p = static_cast<const uint8_t*>(r.k) + off;
-      uint32_t w[EPL / 4];
-      if constexpr (EPL == 8) {
-        uint2 t = *reinterpret_cast<const uint2*>(p);
-        w[0] = t.x;
-        w[1] = t.y;
+  const int stride = gridDim.x * RPB;
+  for (int row0 = blockIdx.x * RPB + threadIdx.x / LPR; row0 < rows; row0 += kRotRows * stride) {
+    uint4 raw[kRotRows];
+    float sc[kRotRows];
+    bool live[kRotRows];
+#pragma unroll
+    for (int i = 0; i < kRotRows; ++i) {
+      const int row = row0 + i * stride;
+      live[i] = false;
+      raw[i] = make_uint4(0u, 0u, 0u, 0u);
+      sc[i] = 0.f;
+      if (row < rows) {
+        const int h = row / r.N, s = row - h * r.N;
+        const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
+        live[i] = r.slot_block[s] != -1;
+        raw[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(r.k) + (srow * D + lane * EPT) * ES);
+        if constexpr (KV == KV_FP8) sc[i] = r.k_scale[srow];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRotRows; ++i) {
+      const int row = row0 + i * stride;
+      if (row >= rows) continue;  // whole rows (and so whole lane groups) skip together
+      const int h = row / r.N, s = row - h * r.N;
+      const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
+      float x[EPT];
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      if constexpr (KV == KV_FP8) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) x[e] = fp8_to_f32(w[e / 4], e % 4) * sc[i];
+      } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+        for (int e = 0; e < EPT / 2; ++e) {
+          x[2 * e] = __uint_as_float(w[e] << 16);
+          x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
       } else {
-        w[0] = *reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) x[e] = __uint_as_float(w[e]);
       }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = fp8_to_f32(w[e / 4], e % 4) * sc;
-    } else {
-      load_row<KV, EPL>(r.k, off, x);
+      for (int e = 0; e < EPT / 2; ++e) {
+        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+        x[2 * e] = x0 * cc[e] - x1 * ss[e];
+        x[2 * e + 1] = x0 * ss[e] + x1 * cc[e];
+      }
+      float nsc = 0.f, rc = 0.f;
+      if constexpr (KV == KV_FP8) {
+        nsc = row_scale<LPR, EPT>(x);
+        rc = scale_rcp(nsc);
+      }
+      if (!live[i]) continue;  // whole rows skip together (after the row's shuffles)
+      store_row<KV, EPT, false>(r.k, srow * D + lane * EPT, x, nsc, rc);  // rotated in float32
+      if constexpr (KV == KV_FP8) {
+        if (lane == 0) r.k_scale[srow] = nsc;
+      }
+      if (h == 0 && lane == 0) r.slot_pos[s] += delta;
     }
-#pragma unroll
-    for (int e = 0; e < EPL / 2; ++e) {
-      float x0 = x[2 * e], x1 = x[2 * e + 1];
-      x[2 * e] = x0 * cc[e] - x1 * ss[e];
-      x[2 * e + 1] = x0 * ss[e] + x1 * cc[e];
-    }
-    float sc = 0.f;
-    if constexpr (KV == KV_FP8) sc = row_scale<EPL>(x);
-    store_row<KV, EPL>(r.k, off, x, sc);
-    if constexpr (KV == KV_FP8) {
-      if (lane16 == 0) r.k_scale[srow] = sc;
-    }
-    if (h == 0 && lane16 == 0) r.slot_pos[s] += delta;
   }
 }
 
@@ -353,16 +457,19 @@ hipError_t fill(void* p, size_t bytes, uint32_t value, hipStream_t s) {
 }
 
 template <int KV, int D>
-hipError_t write_impl(const WriteArgs& a, int chunks, int groups, hipStream_t s) {
-  hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(chunks, groups), dim3(kThreads), 0, s, a);
+hipError_t write_impl(const WriteArgs& a, hipStream_t s) {
+  const int grid = (a.items + 7) / 8 * 8;  // a multiple of 8 for the XCD mapping
+  hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KV, int D>
 hipError_t rerotate_impl(const RingView& r, int delta, hipStream_t s) {
   RopeTable t = make_rope(r.rope_base, r.d);
+  constexpr int LPR = D / (16 / Store<KV>::bytes);
+  constexpr int RPB = kThreads / LPR;
   const int rows = r.H * r.N;
-  int blocks = std::min((rows + kRowsPerPass - 1) / kRowsPerPass, 4096);
+  const int blocks = std::max(1, std::min((rows + RPB * kRotRows - 1) / (RPB * kRotRows), 4096));
   hipLaunchKernelGGL((rerotate_kernel<KV, D>), dim3(blocks), dim3(kThreads), 0, s, r, delta, t);
   return hipGetLastError();
 }
@@ -396,24 +503,19 @@ hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* 
   a.hi_a = std::min(head + n_new, r.N);
   a.lo_b = 0;
   a.hi_b = head + n_new > r.N ? head + n_new - r.N : 0;
-  a.chunks_a = (a.hi_a - 1) / kChunk - a.lo_a / kChunk + 1;
-  const int chunks_b = a.hi_b > 0 ? (a.hi_b - 1) / kChunk + 1 : 0;
+  a.chunks_a = (a.hi_a - 1) / kWChunk - a.lo_a / kWChunk + 1;
+  const int chunks_b = a.hi_b > 0 ? (a.hi_b - 1) / kWChunk + 1 : 0;
   a.use_rope = r.rope_base > 0.f;
   a.rope = make_rope(r.rope_base, r.d);
-  // Heads per workgroup: enough workgroups to cover the chip, and the
-  // chunk's cos/sin table reused over the group.
-  const int chunks = a.chunks_a + chunks_b;
-  int hpg = 1;
-  while (hpg < r.H && chunks * ((r.H + 2 * hpg - 1) / (2 * hpg)) >= 512) hpg *= 2;
-  a.heads_per_group = hpg;
-  const int groups = (r.H + hpg - 1) / hpg;
+  a.chunks = a.chunks_a + chunks_b;
+  a.items = a.chunks * ((r.H + kWHeads - 1) / kWHeads);
   switch (r.kv * 1000 + r.d) {
-    case KV_FP8 * 1000 + 128: return write_impl<KV_FP8, 128>(a, chunks, groups, s);
-    case KV_FP8 * 1000 + 64: return write_impl<KV_FP8, 64>(a, chunks, groups, s);
-    case KV_BF16 * 1000 + 128: return write_impl<KV_BF16, 128>(a, chunks, groups, s);
-    case KV_BF16 * 1000 + 64: return write_impl<KV_BF16, 64>(a, chunks, groups, s);
-    case KV_F32 * 1000 + 128: return write_impl<KV_F32, 128>(a, chunks, groups, s);
-    case KV_F32 * 1000 + 64: return write_impl<KV_F32, 64>(a, chunks, groups, s);
+    case KV_FP8 * 1000 + 128: return write_impl<KV_FP8, 128>(a, s);
+    case KV_FP8 * 1000 + 64: return write_impl<KV_FP8, 64>(a, s);
+    case KV_BF16 * 1000 + 128: return write_impl<KV_BF16, 128>(a, s);
+    case KV_BF16 * 1000 + 64: return write_impl<KV_BF16, 64>(a, s);
+    case KV_F32 * 1000 + 128: return write_impl<KV_F32, 128>(a, s);
+    case KV_F32 * 1000 + 64: return write_impl<KV_F32, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }
