@@ -15,7 +15,9 @@ whole step (240 x 89.73 GFLOP / wall time per chunk); ``ms_per_step`` is
 ms per chunk.  ``roofline`` covers the attention kernel, timed per launch
 with HIP events on the stream it runs on; the write kernel's bandwidth is
 reported beside it.  ``cpu_baseline`` times the float64 oracle on the host
-cores for one layer call (a bounded sample of the same workload).
+cores on a bounded sample of the same workload (layer calls, about ten
+seconds).  ``roofline.traffic`` is the attention kernel's HBM bytes per launch
+from recorded rocprofv3 counter runs, or null if the kernel changed since.
 """
 from __future__ import annotations
 
@@ -45,9 +47,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline() -> dict:
-    """The oracle as it stands, one layer call: write 757 tokens into a full
-    5,788-slot FP8 ring and attend 757 queries over it (40 heads)."""
+def cpu_baseline(min_seconds: float = 10.0, max_calls: int = 12) -> dict:
+    """The oracle as it stands on the host cores, on a bounded sample of the
+    same workload: layer calls (write 757 tokens into a full 5,788-slot FP8
+    ring, then attend 757 queries over it, 40 heads), repeated until about
+    ten seconds of work have been timed."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -61,22 +65,56 @@ def cpu_baseline() -> dict:
     codes |= (rng.integers(0, 2, size=codes.shape, dtype=np.uint8) << 7)
     vcodes = rng.integers(0, 0x7E, size=(H, N, D), dtype=np.uint8)
     scale = (rng.uniform(0.5, 1.5, size=(H, N)) / 100).astype(np.float32)
-    ring = OracleRing.from_arrays(kv_dtype="fp8", rope_base=10000.0, k=codes, v=vcodes, k_scale=scale,
-                                  v_scale=scale.copy(), slot_pos=np.arange(N), slot_block=np.zeros(N, np.int64),
-                                  state=(HIST, HIST, 0, 0, 0))
     _, k = normal_bf16(rng, (NEW, H, D))
     _, v = normal_bf16(rng, (NEW, H, D))
     _, q = normal_bf16(rng, (NEW, H, D))
+    calls, dt = 0, 0.0
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        t0 = time.perf_counter()
-        ring.write(k, v, NEW, HIST, 1)
-        ring_attention(ring, q, HIST, 1, NEW, 0.0)
-        dt = time.perf_counter() - t0
-    return {"value": ATTN_FLOP / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
-            "sample": f"one layer call (write {NEW} tokens + attention {NEW} x {N}, {H} heads, d {D}), "
-                      f"{dt:.2f} s on {used} threads; host has {cores} cores available",
-            "seconds": dt, "ms_per_chunk_extrapolated": dt * 1e3 * PASSES * LAYERS}
+        while calls < max_calls and (dt < min_seconds or calls == 0):
+            ring = OracleRing.from_arrays(kv_dtype="fp8", rope_base=10000.0, k=codes, v=vcodes, k_scale=scale,
+                                          v_scale=scale.copy(), slot_pos=np.arange(N),
+                                          slot_block=np.zeros(N, np.int64), state=(HIST, HIST, 0, 0, 0))
+            t0 = time.perf_counter()
+            ring.write(k, v, NEW, HIST, 1)
+            ring_attention(ring, q, HIST, 1, NEW, 0.0)
+            dt += time.perf_counter() - t0
+            calls += 1
+    per_call = dt / calls
+    return {"value": ATTN_FLOP / per_call / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{calls} layer calls (each: write {NEW} tokens + attention {NEW} x {N}, {H} heads, "
+                      f"d {D}), {dt:.1f} s on {used} threads; host has {cores} cores available",
+            "seconds": dt, "ms_per_chunk_extrapolated": per_call * 1e3 * PASSES * LAYERS}
+
+
+# HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE counter runs (scaled by the same counters on a plain 1 GiB
+# copy), recorded with a hash of the kernel source they were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_attn_fp8_757x5788_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "autoregressive_video_diffusion_ring_amd", "csrc", "chunk_attn.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch from the recorded counter runs, or None when there is
+    no record or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main() -> int:
@@ -202,7 +240,8 @@ def main() -> int:
                    "heads": H, "head_dim": D, "slots": N, "new_tokens": NEW, "layers": LAYERS,
                    "passes": PASSES, "calls_per_chunk": PASSES * LAYERS},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": recorded_traffic(),
                      "kernel": "chunk_attn_kernel<fp8,128>", "us_per_launch": round(attn_us, 2),
                      "flop_per_launch": ATTN_FLOP},
         "write": {"bound": "hbm", "us_per_launch": round(write_us, 2), "bytes_per_launch": WRITE_BYTES,
