@@ -97,7 +97,7 @@ struct AttnArgs {
   RopeTable rope;
 };
 
-// LDS geometry of one tile buffer.
+// LDS geometry of one tile buffer (K rows, then V^T rows).
 template <int KV, int D>
 struct Tile {
   static constexpr int es = KvT<KV>::es;
@@ -107,29 +107,42 @@ struct Tile {
   static constexpr int v_cpr = v_row / 16;
   static constexpr int k_off = 0;
   static constexpr int v_off = kKT * k_row;
-  static constexpr int raw_off = v_off + D * v_row;  // k_scale[64], v_scale[64], block[64]
-  static constexpr int bytes = raw_off + 768;
+  static constexpr int bytes = v_off + D * v_row;
   static constexpr int k_instr = kKT * k_cpr / (kQSub * kWave);  // 16-byte DMA per wave
   static constexpr int v_instr = D * v_cpr / (kQSub * kWave);
+  static constexpr int dma_instr = k_instr + v_instr;
   static_assert(kKT * k_cpr % (kQSub * kWave) == 0 && D * v_cpr % (kQSub * kWave) == 0, "tile split");
 };
 
-// Per-wave factors of one tile, one float per slot: A = c s_k, C = lb / A
-// (lb = log2 s_v, plus the bias when the whole tile takes it) and 1 / s_v.
-constexpr int kFacFloats = 3 * kKT;
+// Per-slot factors of one tile for one key half, written once by one wave of
+// the half a step before the tile is used (words, 64 per array):
+//   A  = c s_k            the logit is A * S' with S' the QK accumulator
+//   C  = log2(s_v) / A    accumulator start, so that A * S' = y0 + log2 s_v
+//   iv = 1 / s_v          weight of P~ in the running sum
+//   kb = block id of the slot (-1: empty)
+// and a summary {any slot valid, all valid, min and max block over valid
+// slots} from which every wave classifies the tile with scalar tests.
+constexpr int kFacA = 0, kFacC = kKT, kFacIv = 2 * kKT, kFacKb = 3 * kKT;
+constexpr int kFacSum = 4 * kKT;
+constexpr int kFacWords = 4 * kKT + 4;
 constexpr float kMinA = 0x1p-90f;  // floor of A, so that C stays finite
+
+// Slot metadata of one tile moves in one 1 KB load: 16-byte chunks 0..15
+// are k_scale, 16..31 v_scale, 32..47 slot_block (FP8); without scales every
+// group of 16 chunks is slot_block.  Chunks 48..63 repeat slot_block, so
+// that all 64 lanes load.
+constexpr int kMetaWords = 256;
+constexpr int kMetaKs = 0, kMetaVs = 64, kMetaKb = 128;
 
 template <int KV, int D>
 struct Stages {
   // Double buffering; each stage holds kps tiles per key half (two when they
-  // fit).  The RoPE tables of the prologue live in the second stage buffer.
-  static constexpr int rope_bytes = (64 + 8 * 64 + 16 * 64) * 8;
+  // fit) and their factor tables.
   static constexpr int need(int kps) {
-    return 2 * kHalves * kps * Tile<KV, D>::bytes + kWaves * kps * kFacFloats * 4 + 256;
+    return 2 * kHalves * kps * (Tile<KV, D>::bytes + kFacWords * 4 + kMetaWords * 4) + 256;
   }
   static constexpr int kps = need(2) <= 160 * 1024 ? 2 : 1;
   static_assert(need(kps) <= 160 * 1024, "LDS budget");
-  static_assert(rope_bytes <= kHalves * kps * Tile<KV, D>::bytes, "RoPE tables fit in one stage");
 };
 
 // Slot (row of the K tile) that lane row m of M-block mb feeds into the QK
@@ -181,22 +194,20 @@ template <int KV, int D>
 struct DmaPlan {
   uint32_t k[Tile<KV, D>::k_instr];  // from the tile's first K row
   uint32_t v[Tile<KV, D>::v_instr];  // from V^T[h][0][first slot of the tile]
-  const uint8_t* meta;               // k_scale / v_scale / slot_block piece of tile 0
+  const uint8_t* meta;               // this lane's metadata chunk of tile 0
 };
-// Per-slot metadata moves in one DMA instruction per wave, so every wave has
-// the same number of loads in flight: FP8 moves 48 chunks (k_scale, v_scale,
-// slot_block; 12 per wave), the other formats 16 (slot_block).
-template <int KV>
-struct MetaSplit {
-  static constexpr int per_wave = KV == KV_FP8 ? 12 : 4;
-  static constexpr int base_chunk = KV == KV_FP8 ? 0 : 32;
-};
+
 
 template <int KV, int D>
 __device__ __forceinline__ DmaPlan<KV, D> dma_plan(const AttnArgs& a, int h, int wq, int lane) {
   using T = Tile<KV, D>;
-  using M = MetaSplit<KV>;
   DmaPlan<KV, D> pl;
+  const int which = KV == KV_FP8 ? min(lane >> 4, 2) : 2;
+  const int j = (lane & 15) * 4;
+  const size_t hs = static_cast<size_t>(h) * a.v_ld + j;
+  pl.meta = which == 0 ? reinterpret_cast<const uint8_t*>(a.k_scale + hs)
+            : which == 1 ? reinterpret_cast<const uint8_t*>(a.v_scale + hs)
+                         : reinterpret_cast<const uint8_t*>(a.slot_block + j);
 #pragma unroll
   for (int j = 0; j < T::k_instr; ++j) {
     const int p = (wq * T::k_instr + j) * kWave + lane;  // LDS chunk index
@@ -209,28 +220,22 @@ __device__ __forceinline__ DmaPlan<KV, D> dma_plan(const AttnArgs& a, int h, int
     const int d = p / T::v_cpr, cp = p % T::v_cpr;
     pl.v[j] = static_cast<uint32_t>(d * a.v_ld * T::es + ((cp ^ v_swz<KV, D>(d)) << 4));
   }
-  const int cc = M::base_chunk + wq * M::per_wave + min(lane, M::per_wave - 1);
-  const int which = cc >> 4, j = (cc & 15) * 4;
-  const size_t hs = static_cast<size_t>(h) * a.v_ld + j;
-  pl.meta = which == 0 ? reinterpret_cast<const uint8_t*>(a.k_scale + hs)
-            : which == 1 ? reinterpret_cast<const uint8_t*>(a.v_scale + hs)
-                         : reinterpret_cast<const uint8_t*>(a.slot_block + j);
   return pl;
 }
 
+// The j-th of this wave's dma_instr loads of one tile (K blocks first).
 template <int KV, int D>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const DmaPlan<KV, D>& pl, int h, int tile,
-                                           uint8_t* buf, int wq, int lane) {
+__device__ __forceinline__ void issue_part(const AttnArgs& a, const DmaPlan<KV, D>& pl, int h, int tile,
+                                           uint8_t* buf, int wq, int j) {
   using T = Tile<KV, D>;
-  using M = MetaSplit<KV>;
-  const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + tile * kKT) * T::k_row;
-#pragma unroll
-  for (int j = 0; j < T::k_instr; ++j) dma16(kb + pl.k[j], buf + T::k_off + (wq * T::k_instr + j) * 1024);
-  const uint8_t* vb = a.v + (static_cast<size_t>(h) * D * a.v_ld + tile * kKT) * T::es;
-#pragma unroll
-  for (int j = 0; j < T::v_instr; ++j) dma16(vb + pl.v[j], buf + T::v_off + (wq * T::v_instr + j) * 1024);
-  if (lane < M::per_wave)
-    dma16(pl.meta + tile * (kKT * 4), buf + T::raw_off + (M::base_chunk + wq * M::per_wave) * 16);
+  if (j < T::k_instr) {
+    const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + tile * kKT) * T::k_row;
+    dma16(kb + pl.k[j], buf + T::k_off + (wq * T::k_instr + j) * 1024);
+  } else {
+    const int jv = j - T::k_instr;
+    const uint8_t* vb = a.v + (static_cast<size_t>(h) * D * a.v_ld + tile * kKT) * T::es;
+    dma16(vb + pl.v[jv], buf + T::v_off + (wq * T::v_instr + jv) * 1024);
+  }
 }
 
 // s_waitcnt vmcnt(N) as a real instruction (gfx9 encoding: vmcnt in bits
@@ -279,8 +284,16 @@ __device__ __forceinline__ int q_dim(int g, int e) {
   else return 2 * e + g;
 }
 
-__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
-  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+// cos and sin of pos * theta_j for the queries: the angle is reduced in
+// float64 to at most half a revolution, then the hardware sine and cosine
+// (which take revolutions) finish it.  Q is rounded to FP8 or BF16 (or kept
+// in float32 for the F32 cache, whose tolerance is far above this error).
+__device__ __forceinline__ void rope_cs_hw(double rev, long long pos, float* c, float* s) {
+  double r = static_cast<double>(pos) * rev;
+  r -= rint(r);
+  const float t = static_cast<float>(r);
+  *s = __builtin_amdgcn_sinf(t);
+  *c = __builtin_amdgcn_cosf(t);
 }
 
 // Four floats to four e4m3 codes written over `old`; both halves of the word
@@ -288,6 +301,21 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
 __device__ __forceinline__ int cvt_fp8x4_over(float a, float b, float c, float d, int old) {
   const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Reduction over the 64 lanes without LDS: quad permutes and row rotations
+// (DPP) inside each row of 16 lanes, then row-pair and half swaps.
+template <bool MAX>
+__device__ __forceinline__ int wave_minmax_i32(int v) {
+  auto op = [](int x, int y) { return MAX ? max(x, y) : min(x, y); };
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(static_cast<int>(r16[0]), static_cast<int>(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(static_cast<int>(r32[0]), static_cast<int>(r32[1]));
 }
 
 template <int KV, int D>
@@ -300,7 +328,12 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   constexpr int kStageBytes = kHalves * KPS * T::bytes;
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) float fac[kWaves * KPS * kFacFloats];
+  // Factor tables of the two stages: [half][kps][kFacWords].
+  __shared__ __attribute__((aligned(16))) float fac0[kHalves * KPS * kFacWords];
+  __shared__ __attribute__((aligned(16))) float fac1[kHalves * KPS * kFacWords];
+  // Slot metadata, two steps ahead: [half][kps][kMetaWords] per array.
+  __shared__ __attribute__((aligned(16))) float meta0[kHalves * KPS * kMetaWords];
+  __shared__ __attribute__((aligned(16))) float meta1[kHalves * KPS * kMetaWords];
   __shared__ float red[kWaves];
 
   const int tid = threadIdx.x;
@@ -326,13 +359,20 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   const int n_steps = (n_local + KPS - 1) / KPS;
   auto tile_of = [&](int li) { return t_begin + 2 * li + kh; };
   auto has_tile = [&](int li) { return li < n_local && tile_of(li) < t_end; };
+  // a tile that exists, reloaded where a load has no tile of its own
+  const int t_safe = min(t_begin, a.n_tiles - 1);
   auto tile_buf = [&](uint8_t* stage, int kk) { return stage + (kh * KPS + kk) * T::bytes; };
+  auto fac_tbl = [&](float* ftab, int kk) { return ftab + (kh * KPS + kk) * kFacWords; };
   const DmaPlan<KV, D> plan = dma_plan<KV, D>(a, h, wq, lane);
   // Every step issues KPS tiles' loads for every wave (past the end a valid
   // tile is reloaded into a slot nobody reads), so wait counts are uniform.
-  auto issue = [&](uint8_t* stage, int st, int kk) {
+  auto issue_j = [&](uint8_t* stage, int st, int kk, int j) {
     const int li = st * KPS + kk;
-    issue_tile<KV, D>(a, plan, h, has_tile(li) ? tile_of(li) : t_begin, tile_buf(stage, kk), wq, lane);
+    issue_part<KV, D>(a, plan, h, has_tile(li) ? tile_of(li) : t_safe, tile_buf(stage, kk), wq, j);
+  };
+  auto issue = [&](uint8_t* stage, int st, int kk) {
+#pragma unroll
+    for (int j = 0; j < T::dma_instr; ++j) issue_j(stage, st, kk, j);
   };
 
   // ---- queries of this lane
@@ -347,10 +387,26 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   const int qb_hi = a.q_block0 + wave_q1 / a.q_block_len;
   const int my_qb = a.q_block0 + (q_ok ? qi : wave_q0) / a.q_block_len;
 
-  // ---- raw Q of this lane, loaded before any tile so that waiting for it
-  //      does not wait for tiles in flight.  Lane group g holds half of the
-  //      query's d values in runs of even length (both members of every RoPE
-  //      pair) for FP8/BF16; for F32 every pair (2e, 2e+1).
+  // ---- slot metadata for the factor tables.  Wave kk < KPS of each half
+  //      builds the table of the half's tile kk of every step from metadata
+  //      it loads into LDS two steps ahead (past the end a valid tile is
+  //      reloaded, so every factor wave issues the same loads).
+  const bool fac_wave = wq < KPS;
+  auto meta_issue = [&](float* mbuf, int st) {
+    const int li = st * KPS + wq;
+    const int tile = has_tile(li) ? tile_of(li) : t_safe;
+    dma16(plan.meta + tile * (kKT * 4), reinterpret_cast<uint8_t*>(mbuf + (kh * KPS + wq) * kMetaWords));
+  };
+  if (fac_wave) {
+    meta_issue(meta0, 0);
+    meta_issue(meta1, 1);
+  }
+
+  // ---- raw Q of this lane.  Lane group g holds half of the query's d values
+  //      in runs of even length (both members of every RoPE pair) for
+  //      FP8/BF16; for F32 every pair (2e, 2e+1).  The first step's tiles
+  //      are issued after these loads, so waiting for Q does not wait for
+  //      them (they go out even for an empty key range, from a valid tile).
   constexpr int kQRaw = KV == KV_F32 ? D / 4 : D / 16;  // 16-byte loads per lane
   v4u qraw[kQRaw];
   {
@@ -365,50 +421,17 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
       qraw[r] = *reinterpret_cast<const v4u*>(qb + byte_off);
     }
   }
-
-  // ---- RoPE frequencies this thread needs for the angle tables below
-  constexpr int kRopeRows = 1 + 8 + 16;
-  constexpr int kRopePer = (kRopeRows * (D / 2) + kThreads - 1) / kThreads;
-  double rev[kRopePer];
 #pragma unroll
-  for (int k = 0; k < kRopePer; ++k) {
-    const int e = tid + k * kThreads;
-    rev[k] = (a.use_rope && e < kRopeRows * (D / 2)) ? a.rope.rev[e % (D / 2)] : 0.0;
-  }
+  for (int kk = 0; kk < KPS; ++kk) issue(st0, 0, kk);
+  // keep the work on Q below these loads, so that waiting for Q does not
+  // hold back their issue
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- start the first step's tiles
-  if (n_steps > 0) {
-#pragma unroll
-    for (int kk = 0; kk < KPS; ++kk) issue(st0, 0, kk);
-  }
-  // ---- RoPE angle tables: e^{i pos theta_j} = e^{i P0 theta_j} e^{i 16 i1 theta_j} e^{i i0 theta_j}
-  //      for pos = P0 + 16 i1 + i0 (angles formed in float64 before sincos).
-  //      They occupy the second stage buffer, which no load touches before
-  //      the first step's barrier.
-  float2* rE0 = reinterpret_cast<float2*>(st1);  // [64]
-  float2* rE1 = rE0 + 64;                         // [8][64]
-  float2* rE2 = rE1 + 8 * 64;                     // [16][64]
-  const long long P0 = static_cast<long long>(a.q_pos0) + q_base;
-  if (a.use_rope) {
-#pragma unroll
-    for (int k = 0; k < kRopePer; ++k) {
-      const int e = tid + k * kThreads;
-      if (e < kRopeRows * (D / 2)) {
-        const int row = e / (D / 2), j = e % (D / 2);
-        const long long pos = row == 0 ? P0 : (row <= 8 ? 16LL * (row - 1) : static_cast<long long>(row - 9));
-        float2 cs;
-        rope_cs_rev(rev[k], pos, &cs.x, &cs.y);
-        float2* dst = row == 0 ? rE0 + j : (row <= 8 ? rE1 + (row - 1) * 64 + j : rE2 + (row - 9) * 64 + j);
-        *dst = cs;
-      }
-    }
-    wait_lgkm0();
-    bare_barrier();
-  }
-
-  // ---- Q: load, rotate, (quantise) into MFMA operand registers
+  // ---- Q: rotate, (quantise) into MFMA operand registers
   QFrag<KV, D> qf;
   float c_mul = a.scale_log2;  // y = c_mul * s_k * S + ...
+  const bool use_rope = a.use_rope != 0;
+  const long long qpos = static_cast<long long>(a.q_pos0) + qi;
   {
     float x[D / 2];
     if constexpr (KV == KV_F32) {
@@ -419,10 +442,11 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         const float x0 = __uint_as_float((e & 1) ? w.z : w.x);
         const float x1 = __uint_as_float((e & 1) ? w.w : w.y);
         float y0 = x0, y1 = x1;
-        if (a.use_rope) {
-          const float2 r = cmul(cmul(rE0[e], rE1[(iq >> 4) * 64 + e]), rE2[(iq & 15) * 64 + e]);
-          y0 = x0 * r.x - x1 * r.y;
-          y1 = x0 * r.y + x1 * r.x;
+        if (use_rope) {
+          float c, sn;
+          rope_cs_hw(a.rope.rev[e], qpos, &c, &sn);
+          y0 = x0 * c - x1 * sn;
+          y1 = x0 * sn + x1 * c;
         }
         x[e] = q_ok ? (g ? y1 : y0) : 0.f;
       }
@@ -434,11 +458,14 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         const float x0 = __uint_as_float(w << 16);
         const float x1 = __uint_as_float(w & 0xFFFF0000u);
         float y0 = x0, y1 = x1;
-        if (a.use_rope) {
-          const int j = q_dim<KV, D>(g, e) >> 1;
-          const float2 r = cmul(cmul(rE0[j], rE1[(iq >> 4) * 64 + j]), rE2[(iq & 15) * 64 + j]);
-          y0 = x0 * r.x - x1 * r.y;
-          y1 = x0 * r.y + x1 * r.x;
+        if (use_rope) {
+          // pair j = q_dim(g, e) / 2: one of two wave-uniform frequencies
+          const int j0 = q_dim<KV, D>(0, e) >> 1, j1 = q_dim<KV, D>(1, e) >> 1;
+          const double rev0 = a.rope.rev[j0], rev1 = a.rope.rev[j1];
+          float c, sn;
+          rope_cs_hw(g ? rev1 : rev0, qpos, &c, &sn);
+          y0 = x0 * c - x1 * sn;
+          y1 = x0 * sn + x1 * c;
         }
         x[e] = q_ok ? y0 : 0.f;
         x[e + 1] = q_ok ? y1 : 0.f;
@@ -487,39 +514,55 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   float msub = 0.f;         // m_run, or 0 while it is -inf: logits are held as y - msub
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial sums of p
   v8i pb = {};  // FP8 P^T operand, rewritten by every tile
-  float* wfac = fac + wave * (KPS * kFacFloats);
 
-  // Per-slot factors of one tile into this wave's own LDS area (lane = slot),
-  // and the wave-uniform tile class: vis (some query of the wave sees some
-  // slot) and fast (every slot visible to every query with one bias value).
-  auto factors = [&](const uint8_t* buf, float* wf, bool& vis, bool& fast) {
-    const int32_t kb = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512)[lane];
+  // ---- factor tables: the table of the half's tile kk of the next step is
+  //      written by wave kk of the half (fac_write, below) from the slot
+  //      metadata loaded here at the start of the current step.
+  auto fac_write = [&](const float* mbuf, float* tbl) {
+    const float* mt = mbuf + (kh * KPS + wq) * kMetaWords;
+    const int kb = reinterpret_cast<const int32_t*>(mt)[kMetaKb + lane];
     const bool kval = kb != -1;
-    vis = __ballot(kval && kb <= qb_hi) != 0ull;
-    const bool all_vis = __ballot(!(kval && kb <= qb_lo)) == 0ull;
-    const bool all_hist = __ballot(!(kval && kb < qb_lo)) == 0ull;
-    const bool all_same = qb_lo == qb_hi && __ballot(!(kval && kb == qb_lo)) == 0ull;
-    fast = all_vis && (all_hist || all_same || a.bias_log2 == 0.f);
     float A = c_mul, lv = 0.f, ivf = 1.f;
     if constexpr (KV == KV_FP8) {
-      const float* raw = reinterpret_cast<const float*>(buf + T::raw_off);
-      const float vs = fmaxf(raw[64 + lane], kMinVScale);
-      A = fmaxf(c_mul * raw[lane], kMinA);
+      const float vs = fmaxf(mt[kMetaVs + lane], kMinVScale);
+      A = fmaxf(c_mul * mt[kMetaKs + lane], kMinA);
       lv = __builtin_amdgcn_logf(vs);
       ivf = __builtin_amdgcn_rcpf(vs);
     }
-    const float lb = (fast && all_hist) ? lv + a.bias_log2 : lv;
-    wf[lane] = A;
-    wf[kKT + lane] = lb * __builtin_amdgcn_rcpf(A);
-    wf[2 * kKT + lane] = ivf;
+    const float rA = __builtin_amdgcn_rcpf(A);
+    tbl[kFacA + lane] = A;
+    tbl[kFacC + lane] = lv * rA;
+    tbl[kFacIv + lane] = ivf;
+    reinterpret_cast<int32_t*>(tbl)[kFacKb + lane] = kb;
+    const uint64_t vb = __ballot(kval);
+    const int kmin = wave_minmax_i32<false>(kval ? kb : INT32_MAX);
+    const int kmax = wave_minmax_i32<true>(kval ? kb : INT32_MIN);
+    if (lane == 0)
+      *reinterpret_cast<v4i*>(tbl + kFacSum) = v4i{vb != 0ull ? 1 : 0, vb == ~0ull ? 1 : 0, kmin, kmax};
+  };
+  // Wave-uniform tile class from the summary: vis (some query of the wave
+  // sees some slot), fast (every slot visible to every query with one bias
+  // value) and hist (fast, and every slot takes the bias).
+  auto classify = [&](const float* tbl, bool& vis, bool& fast, bool& hist) {
+    const v4i sm = *reinterpret_cast<const v4i*>(tbl + kFacSum);
+    const int any = __builtin_amdgcn_readfirstlane(sm.x);
+    const int all = __builtin_amdgcn_readfirstlane(sm.y);
+    const int kmin = __builtin_amdgcn_readfirstlane(sm.z);
+    const int kmax = __builtin_amdgcn_readfirstlane(sm.w);
+    vis = any && kmin <= qb_hi;
+    const bool all_vis = all && kmax <= qb_lo;
+    const bool all_hist = all && kmax < qb_lo;
+    const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
+    fast = all_vis && (all_hist || all_same || a.bias_log2 == 0.f);
+    hist = fast && all_hist;
   };
 
   // S'^T = K Q^T + C: accumulator element i of lane group g is slot
   // 32g + 16mb + i, and starts at that slot's C so that A * S' = y.
-  auto qk = [&](const uint8_t* buf, const float* wf, v16f (&s)[2]) {
+  auto qk = [&](const uint8_t* buf, const float* ctab, v16f (&s)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const float* cf = wf + kKT + 32 * g + 16 * mb;
+      const float* cf = ctab + 32 * g + 16 * mb;
       const v4f c0 = *reinterpret_cast<const v4f*>(cf), c1 = *reinterpret_cast<const v4f*>(cf + 4);
       const v4f c2 = *reinterpret_cast<const v4f*>(cf + 8), c3 = *reinterpret_cast<const v4f*>(cf + 12);
       s[mb] = v16f{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
@@ -552,22 +595,24 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   };
 
   // Softmax update and O^T += V^T P^T for one tile.
-  auto smpv = [&](const uint8_t* buf, const float* wf, v16f (&s)[2], bool fast) {
-    // -- z = A S' - msub = y - msub, masked to -inf
+  auto smpv = [&](const uint8_t* buf, const float* wf, v16f (&s)[2], bool fast, bool hist) {
+    // -- z = A S' (+ bias) - msub = y - msub, masked to -inf.  A fast tile
+    //    takes the bias on every slot or on none.
     const float negm = -msub;
     if (fast) {
+      const float zadd = hist ? negm + a.bias_log2 : negm;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const v4f af = *reinterpret_cast<const v4f*>(wf + 32 * g + 16 * mb + 4 * qq);
-          s[mb][4 * qq + 0] = fmaf(s[mb][4 * qq + 0], af.x, negm);
-          s[mb][4 * qq + 1] = fmaf(s[mb][4 * qq + 1], af.y, negm);
-          s[mb][4 * qq + 2] = fmaf(s[mb][4 * qq + 2], af.z, negm);
-          s[mb][4 * qq + 3] = fmaf(s[mb][4 * qq + 3], af.w, negm);
+          s[mb][4 * qq + 0] = fmaf(s[mb][4 * qq + 0], af.x, zadd);
+          s[mb][4 * qq + 1] = fmaf(s[mb][4 * qq + 1], af.y, zadd);
+          s[mb][4 * qq + 2] = fmaf(s[mb][4 * qq + 2], af.z, zadd);
+          s[mb][4 * qq + 3] = fmaf(s[mb][4 * qq + 3], af.w, zadd);
         }
     } else {
-      const int32_t* kbs = reinterpret_cast<const int32_t*>(buf + T::raw_off + 512);
+      const int32_t* kbs = reinterpret_cast<const int32_t*>(wf + kFacKb);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -612,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
     }
 
     // -- P~ = 2^z; l += P~ / s_v
-    const float* ivfp = wf + 2 * kKT;
+    const float* ivfp = wf + kFacIv;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -675,42 +720,45 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   };
 
   // One pipeline step: the KPS tiles of stage `cur` are computed while the
-  // next step's tiles are loaded into `nxt`.  The loads are issued between
-  // the tiles' matrix work rather than all at once, so that no wave stalls
-  // on a full load queue.
-  auto step = [&](uint8_t* cur, uint8_t* nxt, int st) {
+  // next step's tiles are loaded into `nxt` and the factor waves fill the
+  // next step's tables.  A wave issues its loads of next-step tile kk right
+  // after the QK MFMAs of current tile kk, so that the issue (which stalls
+  // while the load queue is busy) overlaps matrix work.
+  auto step = [&](uint8_t* cur, uint8_t* nxt, float* fcur, float* fnxt, float* mcur, float* mnxt, int st) {
     wait_vm<0>();    // this wave's loads of this step have landed
+    wait_lgkm0();    // and its table writes are done
     bare_barrier();  // every wave's: visible to all; every wave is done with `nxt`
     const bool more = st + 1 < n_steps;
+    if (fac_wave && st + 2 < n_steps) meta_issue(mcur, st + 2);
     if (!wave_active) {
       if (more) {
 #pragma unroll
         for (int kk = 0; kk < KPS; ++kk) issue(nxt, st + 1, kk);
       }
-      return;
-    }
-    bool vis[KPS], fast[KPS];
+    } else {
+      bool vis[KPS], fast[KPS], hist[KPS];
 #pragma unroll
-    for (int kk = 0; kk < KPS; ++kk) {
-      vis[kk] = false;
-      fast[kk] = false;
-      if (has_tile(st * KPS + kk)) factors(tile_buf(cur, kk), wfac + kk * kFacFloats, vis[kk], fast[kk]);
-    }
-    v16f s[KPS][2];
+      for (int kk = 0; kk < KPS; ++kk) {
+        classify(fac_tbl(fcur, kk), vis[kk], fast[kk], hist[kk]);
+        vis[kk] = vis[kk] && has_tile(st * KPS + kk);
+      }
 #pragma unroll
-    for (int kk = 0; kk < KPS; ++kk) {
-      if (vis[kk]) qk(tile_buf(cur, kk), wfac + kk * kFacFloats, s[kk]);
-      if (kk == 0 && more) issue(nxt, st + 1, 0);
+      for (int kk = 0; kk < KPS; ++kk) {
+        const float* tbl = fac_tbl(fcur, kk);
+        // QK runs even for a tile the wave cannot see (its result is then
+        // unused): its LDS reads then overlap those of the tile summary.
+        v16f sc[2];
+        qk(tile_buf(cur, kk), tbl + kFacC, sc);
+        if (more) issue(nxt, st + 1, kk);
+        if (vis[kk]) smpv(tile_buf(cur, kk), tbl, sc, fast[kk], hist[kk]);
+      }
     }
-#pragma unroll
-    for (int kk = 0; kk < KPS; ++kk) {
-      if (vis[kk]) smpv(tile_buf(cur, kk), wfac + kk * kFacFloats, s[kk], fast[kk]);
-      if (kk + 1 < KPS && more) issue(nxt, st + 1, kk + 1);
-    }
+    if (fac_wave && more) fac_write(mnxt, fac_tbl(fnxt, wq));
   };
+  if (n_steps > 0 && fac_wave) fac_write(meta0, fac_tbl(fac0, wq));
   for (int st = 0; st < n_steps; st += 2) {
-    step(st0, st1, st);
-    if (st + 1 < n_steps) step(st1, st0, st + 1);
+    step(st0, st1, fac0, fac1, meta0, meta1, st);
+    if (st + 1 < n_steps) step(st1, st0, fac1, fac0, meta1, meta0, st + 1);
   }
 
   // ---- merge the two key halves of every query sub-tile through LDS
