@@ -387,15 +387,20 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   const int qb_hi = a.q_block0 + wave_q1 / a.q_block_len;
   const int my_qb = a.q_block0 + (q_ok ? qi : wave_q0) / a.q_block_len;
 
-  // ---- slot metadata for the factor tables.  Wave kk < KPS of each half
-  //      builds the table of the half's tile kk of every step from metadata
-  //      it loads into LDS two steps ahead (past the end a valid tile is
-  //      reloaded, so every factor wave issues the same loads).
-  const bool fac_wave = wq < KPS;
+  // ---- slot metadata for the factor tables.  Wave f = wq of key half 0
+  //      builds table f (tile f % KPS of half f / KPS) of every step, from
+  //      metadata it loads into LDS two steps ahead (past the end a valid
+  //      tile is reloaded, so every factor wave issues the same loads).  The
+  //      work sits in half 0 because its waves are the older ones on each
+  //      SIMD, which issue first and otherwise wait at the step barrier.
+  const int fac_id = wq;
+  const bool fac_wave = kh == 0 && fac_id < kHalves * KPS;
+  const int fh = fac_id / KPS, fk = fac_id % KPS;
   auto meta_issue = [&](float* mbuf, int st) {
-    const int li = st * KPS + wq;
-    const int tile = has_tile(li) ? tile_of(li) : t_safe;
-    dma16(plan.meta + tile * (kKT * 4), reinterpret_cast<uint8_t*>(mbuf + (kh * KPS + wq) * kMetaWords));
+    const int li = st * KPS + fk;
+    const int tf = t_begin + 2 * li + fh;
+    const int tile = li < n_local && tf < t_end ? tf : t_safe;
+    dma16(plan.meta + tile * (kKT * 4), reinterpret_cast<uint8_t*>(mbuf + fac_id * kMetaWords));
   };
   if (fac_wave) {
     meta_issue(meta0, 0);
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   //      written by wave kk of the half (fac_write, below) from the slot
   //      metadata loaded here at the start of the current step.
   auto fac_write = [&](const float* mbuf, float* tbl) {
-    const float* mt = mbuf + (kh * KPS + wq) * kMetaWords;
+    const float* mt = mbuf + fac_id * kMetaWords;
     const int kb = reinterpret_cast<const int32_t*>(mt)[kMetaKb + lane];
     const bool kval = kb != -1;
     float A = c_mul, lv = 0.f, ivf = 1.f;
@@ -753,9 +758,9 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
         if (vis[kk]) smpv(tile_buf(cur, kk), tbl, sc, fast[kk], hist[kk]);
       }
     }
-    if (fac_wave && more) fac_write(mnxt, fac_tbl(fnxt, wq));
+    if (fac_wave && more) fac_write(mnxt, fnxt + fac_id * kFacWords);
   };
-  if (n_steps > 0 && fac_wave) fac_write(meta0, fac_tbl(fac0, wq));
+  if (n_steps > 0 && fac_wave) fac_write(meta0, fac0 + fac_id * kFacWords);
   for (int st = 0; st < n_steps; st += 2) {
     step(st0, st1, fac0, fac1, meta0, meta1, st);
     if (st + 1 < n_steps) step(st1, st0, fac1, fac0, meta1, meta0, st + 1);
