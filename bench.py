@@ -12,12 +12,22 @@ Q/K/V come from a pool of 16 synthetic N(0,1) bf16 sets (372 MB).
 
 Prints ONE JSON line on stdout.  ``value`` is chunk-attention TFLOP/s over the
 whole step (240 x 89.73 GFLOP / wall time per chunk); ``ms_per_step`` is
-ms per chunk.  ``roofline`` covers the attention kernel, timed per launch
-with HIP events on the stream it runs on; the write kernel's bandwidth is
-reported beside it.  ``cpu_baseline`` times the float64 oracle on the host
-cores on a bounded sample of the same workload (layer calls, about ten
-seconds).  ``roofline.traffic`` is the attention kernel's HBM bytes per launch
-from recorded rocprofv3 counter runs, or null if the kernel changed since.
+ms per chunk.  ``roofline`` covers the attention kernel, timed with HIP events
+on the stream it runs on, around layer 0's launches of every pass in the timed
+chunks; the write and rerotate kernels' bandwidths are reported beside it.
+``roofline.traffic`` is the attention kernel's HBM bytes per launch from
+recorded rocprofv3 counter runs, or null if the kernel changed since.
+``cpu_baseline`` times the float64 oracle on the host cores on a bounded sample
+of the same workload (layer calls, about ten seconds).  ``joint_av`` times the
+four paths of a joint audio-video block (StreamLTX project page, Training:
+one-second blocks of 1,152 video and 25 audio tokens, 10 blocks cached, 32
+heads, bf16, block-causal), each with the last block's queries and with all
+ten blocks' queries.
+
+``--longrun K`` instead runs K chunks of the long-run schedule (a position
+reset every 300 chunks by a delta rotation of all 60 rings, ten cache-bias
+ramps 0, -2, -4, -2, 0) and prints one JSON line with the sustained ms/chunk
+(median and p99).
 """
 from __future__ import annotations
 
@@ -40,7 +50,10 @@ WRITE_BYTES = (2 * NEW * H * D * 2            # K and V in, bf16
                + 2 * NEW * 4)                 # slot_pos, slot_block
 REROT_BYTES = 2 * (H * N * D + H * N * 4) + N * 4 + 2 * N * 4  # codes+scales in/out, block read, pos rw
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+AV_H, AV_BLOCKS, AV_VIDEO, AV_AUDIO = 32, 10, 1152, 25
+RESET_EVERY, RAMPS, RAMP_FIRST, RAMP_SPACING, RAMP_DEPTH = 300, 10, 150, 200, 4.0
 
 
 def log(*a):
@@ -94,6 +107,136 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_attn_fp8_757x5788_traffic.t
 KERNEL_SOURCE = os.path.join(ROOT, "autoregressive_video_diffusion_ring_amd", "csrc", "chunk_attn.hip")
 
 
+def timed_us(fn, stream, reps: int = 20, warm: int = 3) -> float:
+    """Median of `reps` launches of fn, each bracketed by HIP events on `stream`."""
+    import torch
+    for _ in range(warm):
+        fn()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return t[len(t) // 2]
+
+
+def joint_av(dev, stream) -> dict:
+    """The four attention paths of one joint audio-video block: bf16 rings of
+    ten one-second blocks (video 1,152 tokens per block, audio 25), 32 heads,
+    d 128, no RoPE, bias 0.  Work per path is 4*H*d per visible (query, slot)
+    pair; bytes are the ring's K and V once plus Q in and O out."""
+    import torch
+
+    from autoregressive_video_diffusion_ring_amd import Ring
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    rnd = lambda n: torch.randn((n, AV_H, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rings, qs = {}, {}
+    for name, blen in (("video", AV_VIDEO), ("audio", AV_AUDIO)):
+        r = Ring(blen * AV_BLOCKS, AV_H, D, "bf16", 0.0, device=dev)
+        for b in range(AV_BLOCKS):
+            r.write(rnd(blen), rnd(blen), blen * b, b)
+            if b < AV_BLOCKS - 1:
+                r.advance(blen)
+        rings[name] = (r, blen)
+        qs[name] = rnd(blen * AV_BLOCKS)
+    res = {}
+    for qn, kn in (("video", "video"), ("audio", "audio"), ("video", "audio"), ("audio", "video")):
+        ring, kblen = rings[kn]
+        qblen = rings[qn][1]
+        for mode in ("last_block", "all_blocks"):
+            q = qs[qn][(AV_BLOCKS - 1) * qblen:].contiguous() if mode == "last_block" else qs[qn]
+            qb0 = AV_BLOCKS - 1 if mode == "last_block" else 0
+            n_q = q.shape[0]
+            out = torch.empty_like(q)
+            need = ring.workspace_bytes(n_q)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            us = timed_us(lambda: ring.attention(q, 0, qb0, qblen, 0.0, out=out, workspace=ws, stream=stream), stream)
+            blocks = [AV_BLOCKS - 1] if mode == "last_block" else list(range(AV_BLOCKS))
+            pairs = sum(qblen * (b + 1) * kblen for b in blocks)
+            flop = 4.0 * AV_H * D * pairs
+            nbytes = 2 * AV_H * ring.N * D * 2 + 2 * n_q * AV_H * D * 2
+            tf, gbs = flop / (us * 1e-6) / 1e12, nbytes / (us * 1e-6) / 1e9
+            res[f"{qn[0]}->{kn[0]} {mode}"] = {
+                "queries": n_q, "slots": ring.N, "us": round(us, 2), "gflop": round(flop / 1e9, 3),
+                "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "mbytes": round(nbytes / 1e6, 2), "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
+def chunk_pos0(t: int) -> int:
+    """First position of chunk t; every reset rebases the cache to 0..N-1."""
+    return NEW * t if t < RESET_EVERY else N + NEW * (t % RESET_EVERY)
+
+
+def bias_at(t: int) -> float:
+    shape = (0.0, -RAMP_DEPTH / 2, -RAMP_DEPTH, -RAMP_DEPTH / 2, 0.0)
+    for k in range(RAMPS):
+        s0 = RAMP_FIRST + k * RAMP_SPACING
+        if s0 <= t < s0 + len(shape):
+            return shape[t - s0]
+    return 0.0
+
+
+def longrun(n_chunks: int) -> dict:
+    """Sustained chunks of the long-run schedule from an empty cache: each
+    chunk is 4 passes x 60 layers of write + attention, then 60 advances;
+    before every 300th chunk all 60 rings are rerotated so that the oldest
+    cached position becomes 0; the cache bias follows ten ramps."""
+    import torch
+
+    from autoregressive_video_diffusion_ring_amd import Ring, rc_cache_write, rc_chunk_attention, rc_ring_advance
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    rings = [Ring(N, H, D, "fp8", 10000.0, device=dev) for _ in range(LAYERS)]
+    pool = [[torch.randn((NEW, H, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+             for _ in range(3)] for _ in range(POOL)]
+    out = torch.empty((NEW, H, D), dtype=torch.bfloat16, device=dev)
+    structs = [r.struct for r in rings]
+    torch.cuda.synchronize()
+    evs, resets = [], []
+    for t in range(n_chunks):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if t > 0 and t % RESET_EVERY == 0:
+            delta = -(chunk_pos0(t - 1) + NEW - N)  # oldest cached position -> 0 (the ring is full)
+            for r in rings:
+                r.rerotate(delta)
+            resets.append(t)
+        pos0, bias = chunk_pos0(t), bias_at(t)
+        for p in range(PASSES):
+            for layer in range(LAYERS):
+                q, k, v = pool[(240 * t + 60 * p + layer) % POOL]
+                rc_cache_write(structs[layer], k, v, NEW, pos0, t, sptr)
+                rc_chunk_attention(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, out, None, None, 0, sptr)
+        for s in structs:
+            rc_ring_advance(s, NEW)
+        e1.record(stream)
+        evs.append((e0, e1))
+        if t % 100 == 99:
+            torch.cuda.synchronize()
+            log(f"[longrun] {t + 1} chunks")
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    steady = sorted(m for i, m in enumerate(ms) if i >= 8 and i not in resets)
+    full = sorted(ms[8:])
+    pick = lambda v, f: v[min(len(v) - 1, int(f * len(v)))]
+    return {"metric": "sustained ms/chunk, long-run schedule (757 new x 5788-slot fp8 ring, 60 layers)",
+            "value": round(pick(full, 0.5), 4), "unit": "ms", "higher_is_better": False,
+            "chunks": n_chunks, "p99_ms": round(pick(full, 0.99), 4), "mean_ms": round(sum(full) / len(full), 4),
+            "steady_median_ms": round(pick(steady, 0.5), 4),
+            "reset_chunk_ms": [round(ms[i], 3) for i in resets],
+            "fill_chunks_ms": [round(m, 3) for m in ms[:8]],
+            "dtype": "fp8", "data": "synthetic", "n_gpus": 1}
+
+
 def kernel_source_hash() -> str:
     import hashlib
     with open(KERNEL_SOURCE, "rb") as f:
@@ -125,6 +268,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--no-joint-av", action="store_true", help="skip the joint audio-video paths")
+    ap.add_argument("--longrun", type=int, default=0, metavar="K",
+                    help="run K chunks of the long-run schedule instead and print that line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -136,6 +282,11 @@ def main() -> int:
     import torch
 
     from autoregressive_video_diffusion_ring_amd import Ring, rc_cache_write, rc_chunk_attention, rc_ring_advance
+
+    if args.longrun > 0:
+        torch.cuda.set_device(0)
+        print(json.dumps(longrun(args.longrun)), flush=True)
+        return 0
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -168,14 +319,17 @@ def main() -> int:
             for layer in range(LAYERS):
                 q, k, v = pool[(240 * t + 60 * p + layer) % POOL]
                 s = structs[layer]
-                if timed:
+                # kernel durations: HIP events around layer 0's two launches
+                # of every pass (sampling keeps their cost out of the step)
+                ev = timed and layer == 0
+                if ev:
                     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                     e0.record(stream)
                 rc_cache_write(s, k, v, NEW, pos0, blk, sptr)
-                if timed:
+                if ev:
                     e1.record(stream)
                 rc_chunk_attention(s, q, NEW, pos0, blk, NEW, 0.0, 0.0, out, None, None, 0, sptr)
-                if timed:
+                if ev:
                     e2.record(stream)
                     ev_write.append((e0, e1))
                     ev_attn.append((e1, e2))
@@ -251,7 +405,11 @@ def main() -> int:
                      "achieved": round(REROT_BYTES / (rot_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(REROT_BYTES / (rot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
+        "joint_av": None,
     }
+    if not args.no_joint_av:
+        log("[bench] joint audio-video paths")
+        result["joint_av"] = joint_av(dev, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (one layer call)")
         result["cpu_baseline"] = cpu_baseline()
