@@ -10,15 +10,17 @@
 // Write layout: the written range [head, head + n) mod N is cut into at most
 // two linear slot ranges, and each range into 32-slot chunks aligned to
 // multiples of 32.  One workgroup handles one chunk for kWHeads heads:
-//  * cos/sin of every (slot, pair) of the chunk go to LDS once, built from
-//    one float64-reduced angle per frequency at the chunk's first position
-//    times small-angle factors, and are reused for every head;
 //  * a row (one token of one head, d elements) is handled by 16 lanes with
 //    d/16 contiguous elements each, so a row's loads and stores are whole
-//    contiguous cache rows;
-//  * V is quantised the same way, transposed through LDS and stored to the
-//    [H][d][v_ld] layout as 16-byte pieces (chunks start on a multiple of 32
-//    and v_ld is a multiple of 64, so pieces are aligned).
+//    contiguous cache rows; a thread takes 4 consecutive slots of one head;
+//  * each RoPE angle is reduced in float64 to at most half a revolution and
+//    finished by the hardware sine and cosine (which take revolutions; their
+//    error on that range is about 2^-23, the same as float32 rounding of the
+//    angle itself);
+//  * V is quantised the same way, transposed through LDS (a thread writes the
+//    4 slots of one d as one word) and stored to the [H][d][v_ld] layout as
+//    16-byte pieces (chunks start on a multiple of 32 and v_ld is a multiple
+//    of 64, so pieces are aligned).
 #include <algorithm>
 #include <cmath>
 
@@ -33,7 +35,9 @@ constexpr int kWChunk = 32;                  // slots per write workgroup
 constexpr int kWHeads = 2;                   // heads per write workgroup
 constexpr int kLanesPerRow = 16;
 constexpr int kRowGroups = kThreads / kLanesPerRow;
-constexpr int kRowsPerThread = kWChunk * kWHeads / kRowGroups;
+constexpr int kRowsPerThread = kWChunk * kWHeads / kRowGroups;  // consecutive slots
+constexpr int kSlotGroups = kWChunk / kRowsPerThread;  // row groups per head
+static_assert(kRowsPerThread == 4 && kSlotGroups * kWHeads == kRowGroups, "thread -> rows");
 
 template <int KV>
 struct Store;
@@ -180,20 +184,18 @@ __device__ __forceinline__ float row_scale(const float* x) {
   float a = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
-  a = group_max<LANES>(a);
-  return a / 448.0f;
+  if constexpr (LANES == 4 || LANES == 8 || LANES == 16) a = group_max_dpp<LANES>(a);  // rows are aligned lane groups
+  else a = group_max<LANES>(a);
+  return div448(a);
 }
 
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   constexpr int EPL = D / kLanesPerRow;
   constexpr int ES = Store<KV>::bytes;
-  constexpr int RJ = D / 2;  // RoPE pairs
-  __shared__ float2 cs[kWChunk][RJ];
-  __shared__ float2 e0[RJ], e1[kWChunk / 8][RJ], e2[8][RJ];
-  // V^T rows of the chunk, padded by 4 bytes against bank conflicts of the
-  // transposing byte writes (rows are read back as 4-byte words)
-  constexpr int RS = kWChunk * ES + 4;
+  // V^T rows of the chunk: row (head, j) holds the chunk's slots, padded by
+  // 4 slots against bank conflicts of the transposing writes
+  constexpr int RS = (kWChunk + 4) * ES;
   __shared__ __attribute__((aligned(16))) uint8_t vt[kWHeads * D * RS];
 
   const int tid = threadIdx.x;
@@ -221,17 +223,17 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
     int t = s - a.head;
     return t < 0 ? t + N : t;
   };
-  const int h0 = group * kWHeads;
   const int piece = tid % kLanesPerRow;
   const int rg = tid / kLanesPerRow;
+  const int hh = rg / kSlotGroups;                       // head of this thread's rows
+  const int sl0 = (rg % kSlotGroups) * kRowsPerThread;   // first of its 4 slots
+  const int h = group * kWHeads + hh;
 
   // ---- all input loads first
   Raw<KV, EPL> rk[kRowsPerThread], rv[kRowsPerThread];
 #pragma unroll
   for (int i = 0; i < kRowsPerThread; ++i) {
-    const int row = rg + i * kRowGroups;
-    const int sl = row % kWChunk, hh = row / kWChunk;
-    const int s = base + sl, h = h0 + hh;
+    const int s = base + sl0 + i;
 #pragma unroll
     for (int w = 0; w < Raw<KV, EPL>::words; ++w) rk[i].w[w] = rv[i].w[w] = 0u;
     if (s >= lo && s < hi && h < H) {
@@ -240,6 +242,9 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
       load_raw<KV, EPL>(a.v_new, off, rv[i]);
     }
   }
+  double rev[EPL / 2];
+#pragma unroll
+  for (int e = 0; e < EPL / 2; ++e) rev[e] = a.rope.rev[piece * (EPL / 2) + e];
 
   // ---- slot metadata (first head group only)
   if (group == 0 && tid < kWChunk) {
@@ -249,39 +254,16 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
       a.r.slot_block[s] = a.block_id;
     }
   }
+  // position of this thread's first slot: the chunk's slots from lo on hold
+  // consecutive tokens (rows outside [lo, hi) are computed but not stored)
+  const long long pos_first = static_cast<long long>(a.pos0) + token_of(lo) + (base + sl0 - lo);
 
-  // ---- RoPE table of the chunk, while the loads are in flight:
-  //      e^{i (P + t) theta_j} = e^{i P theta_j} e^{i 8 (t / 8) theta_j} e^{i (t % 8) theta_j}
-  //      with P the position of the chunk's first slot (the first factor's
-  //      angle reduced in float64).
-  if (a.use_rope) {
-    const long long P = static_cast<long long>(a.pos0) + token_of(lo) - (lo - base);
-    constexpr int kE = RJ * (1 + kWChunk / 8 + 8);
-    for (int e = tid; e < kE; e += kThreads) {
-      const int row = e / RJ, j = e % RJ;
-      const long long pos = row == 0 ? P : (row <= kWChunk / 8 ? 8LL * (row - 1) : static_cast<long long>(row - 1 - kWChunk / 8));
-      float2 v;
-      rope_cs(a.rope, j, pos, &v.x, &v.y);
-      if (row == 0) e0[j] = v;
-      else if (row <= kWChunk / 8) e1[row - 1][j] = v;
-      else e2[row - 1 - kWChunk / 8][j] = v;
-    }
-    __syncthreads();
-    for (int e = tid; e < kWChunk * RJ; e += kThreads) {
-      const int t = e / RJ, j = e % RJ;
-      const float2 p = e0[j], q = e1[t / 8][j], r = e2[t % 8][j];
-      const float2 pq = make_float2(p.x * q.x - p.y * q.y, p.x * q.y + p.y * q.x);
-      cs[t][j] = make_float2(pq.x * r.x - pq.y * r.y, pq.x * r.y + pq.y * r.x);
-    }
-    __syncthreads();
-  }
-
-  // ---- rows: rotate, quantise, store K; quantise V into LDS (transposed)
+  // ---- rows: rotate, quantise, store K; quantise V
+  uint32_t vcode[kRowsPerThread][EPL / 4];  // FP8 codes of V (ES == 1)
+  float vval[kRowsPerThread][ES == 1 ? 1 : EPL];  // V values (BF16 / F32 rings)
 #pragma unroll
   for (int i = 0; i < kRowsPerThread; ++i) {
-    const int row = rg + i * kRowGroups;
-    const int sl = row % kWChunk, hh = row / kWChunk;
-    const int s = base + sl, h = h0 + hh;
+    const int s = base + sl0 + i;
     const bool valid = s >= lo && s < hi && h < H;
     float xk[EPL], xv[EPL];
     unpack<KV, EPL>(rk[i], xk);
@@ -289,10 +271,13 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
     if (a.use_rope) {
 #pragma unroll
       for (int e = 0; e < EPL / 2; ++e) {
-        const float2 t = cs[sl][piece * (EPL / 2) + e];
+        double r = static_cast<double>(pos_first + i) * rev[e];
+        r -= rint(r);
+        const float t = static_cast<float>(r);
+        const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
         const float x0 = xk[2 * e], x1 = xk[2 * e + 1];
-        xk[2 * e] = x0 * t.x - x1 * t.y;
-        xk[2 * e + 1] = x0 * t.y + x1 * t.x;
+        xk[2 * e] = x0 * cs - x1 * sn;
+        xk[2 * e + 1] = x0 * sn + x1 * cs;
       }
     }
     float ks = 0.f, vs = 0.f, krc = 0.f, vrc = 0.f;
@@ -314,19 +299,29 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
         }
       }
     }
-    // V^T in LDS: row (hh, j) at (hh * D + j) * RS, slot sl at sl * ES
-    uint8_t* vcol = vt + static_cast<size_t>(hh) * D * RS + (piece * EPL) * RS + sl * ES;
     if constexpr (KV == KV_FP8) {
-      uint32_t w[EPL / 4];
-      encode_fp8<EPL, true>(xv, vs, vrc, w);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) vcol[e * RS] = static_cast<uint8_t>(w[e / 4] >> (8 * (e % 4)));
-    } else if constexpr (KV == KV_BF16) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) *reinterpret_cast<uint16_t*>(vcol + e * RS) = f32_to_bf16(xv[e]);
+      encode_fp8<EPL, true>(xv, vs, vrc, vcode[i]);
     } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) *reinterpret_cast<float*>(vcol + e * RS) = xv[e];
+      for (int e = 0; e < EPL; ++e) vval[i][e] = xv[e];
+    }
+  }
+  // ---- V^T in LDS: row (hh, j) at (hh * D + j) * RS; this thread's 4 slots of
+  //      each of its d values j go in as one piece (4 codes, 4 bf16 or 4 floats)
+  uint8_t* vrow = vt + (static_cast<size_t>(hh) * D + piece * EPL) * RS + sl0 * ES;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    uint8_t* dst = vrow + e * RS;
+    if constexpr (KV == KV_FP8) {
+      // byte e % 4 of word e / 4 of each row, gathered into one word
+      const int sh = 8 * (e % 4);
+      const uint32_t b0 = (vcode[0][e / 4] >> sh) & 0xFFu, b1 = (vcode[1][e / 4] >> sh) & 0xFFu;
+      const uint32_t b2 = (vcode[2][e / 4] >> sh) & 0xFFu, b3 = (vcode[3][e / 4] >> sh) & 0xFFu;
+      *reinterpret_cast<uint32_t*>(dst) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    } else if constexpr (KV == KV_BF16) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(vval[0][e], vval[1][e]), pack_bf16x2(vval[2][e], vval[3][e]));
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(vval[0][e], vval[1][e], vval[2][e], vval[3][e]);
     }
   }
   __syncthreads();
@@ -335,14 +330,14 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   constexpr int kSlotsPerPiece = 16 / ES;
   constexpr int kPiecesPerRow = kWChunk / kSlotsPerPiece;
   for (int u = tid; u < kWHeads * D * kPiecesPerRow; u += kThreads) {
-    const int hh = u / (D * kPiecesPerRow);
-    const int rem = u - hh * (D * kPiecesPerRow);
+    const int hq = u / (D * kPiecesPerRow);
+    const int rem = u - hq * (D * kPiecesPerRow);
     const int j = rem / kPiecesPerRow, w = rem - j * kPiecesPerRow;
-    const int h = h0 + hh;
-    if (h >= H) continue;
+    const int hd = group * kWHeads + hq;
+    if (hd >= H) continue;
     const int s0 = base + w * kSlotsPerPiece;
-    const uint8_t* src = vt + (static_cast<size_t>(hh) * D + j) * RS + w * 16;
-    uint8_t* dst = static_cast<uint8_t*>(a.r.v) + ((static_cast<size_t>(h) * D + j) * a.r.v_ld + s0) * ES;
+    const uint8_t* src = vt + (static_cast<size_t>(hq) * D + j) * RS + w * 16;
+    uint8_t* dst = static_cast<uint8_t*>(a.r.v) + ((static_cast<size_t>(hd) * D + j) * a.r.v_ld + s0) * ES;
     if (s0 >= lo && s0 + kSlotsPerPiece <= hi) {
       const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
       *reinterpret_cast<uint4*>(dst) = make_uint4(s32[0], s32[1], s32[2], s32[3]);

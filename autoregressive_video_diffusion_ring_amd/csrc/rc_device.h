@@ -87,4 +87,33 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Maximum over aligned groups of W = 4, 8 or 16 lanes with DPP lane moves
+// inside each row of 16 lanes (no LDS round trips): two quad permutes, then
+// the half-row mirror (lane i <-> 7 - i) and the row mirror (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int W>
+__device__ __forceinline__ float group_max_dpp(float v) {
+  static_assert(W == 4 || W == 8 || W == 16, "DPP group size");
+  v = fmaxf(v, dpp_mov<0xB1>(v));  // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_mov<0x4E>(v));  // quad_perm 2,3,0,1
+  if constexpr (W >= 8) v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+  if constexpr (W >= 16) v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+  return v;
+}
+
+// a / 448 rounded to nearest (IEEE float32 division) from the reciprocal and
+// one FMA correction; checked against the division for every positive float
+// whose quotient is a normal number, which holds for a >= 2^-100 (smaller a
+// takes the division).
+__device__ __forceinline__ float div448(float a) {
+  constexpr float y = 1.0f / 448.0f;
+  const float q0 = a * y;
+  float q = fmaf(fmaf(-q0, 448.0f, a), y, q0);
+  if (__ballot(!(a >= 0x1p-100f)) != 0ull) q = a >= 0x1p-100f ? q : a / 448.0f;  // skipped by the wave
+  return q;                                                                      // unless a lane needs it
+}
+
 }  // namespace rc
