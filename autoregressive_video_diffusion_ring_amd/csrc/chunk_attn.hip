@@ -711,13 +711,15 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int slot = 32 * g + 16 * mb + e;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int slot = 32 * g + 16 * mb + 4 * e4;  // one 16-byte chunk: slots slot .. slot + 3
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const int d = 32 * db + n;
-            const float av = *reinterpret_cast<const float*>(buf + v_addr<KV, D>(d, slot >> 2) + (slot & 3) * 4);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, s[mb][e], o[db], 0, 0, 0);
+            const v4f av = *reinterpret_cast<const v4f*>(buf + v_addr<KV, D>(d, slot >> 2));
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k], s[mb][4 * e4 + k], o[db], 0, 0, 0);
           }
         }
       }
