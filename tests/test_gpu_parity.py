@@ -179,6 +179,43 @@ def test_attention_ragged_multiblock(kv, d):
     assert_attention_close(out, ref2, kv)
 
 
+def test_attention_zero_rows_and_scale_spread():
+    """Degenerate and extreme rows: all-zero K rows (scale 0), all-zero V rows
+    (scale 0: the row still carries its softmax weight, so the sum must count
+    it), and V rows scaled by 2^10 and 2^-10 so that per-slot V scales span
+    2^20.  Powers of two keep the bf16 inputs exact."""
+    banner("attention: fp8 with zero K / V rows and V scales spread over 2^20")
+    rng = np.random.default_rng(33)
+    N, H, d = 320, 4, 128
+    g, o = make_pair(N, H, d, "fp8", 10000.0)
+    for b, (n, p0) in enumerate([(120, 0), (110, 120), (80, 230)]):
+        kt, k = inputs(rng, "fp8", (n, H, d))
+        vt, v = inputs(rng, "fp8", (n, H, d))
+        pick = rng.integers(0, 6, size=(n, H))
+        for sel, kind in ((pick == 0, "k0"), (pick == 1, "v0"), (pick == 2, "vbig"), (pick == 3, "vsmall")):
+            m = torch.from_numpy(sel).to(DEV)
+            if kind == "k0":
+                kt[m] = 0
+                k[sel] = 0.0
+            elif kind == "v0":
+                vt[m] = 0
+                v[sel] = 0.0
+            else:
+                f = 1024.0 if kind == "vbig" else 1.0 / 1024.0
+                vt[m] = vt[m] * f
+                v[sel] = v[sel] * f
+        g.write(kt, vt, p0, b)
+        o.write(k, v, n, p0, b)
+        g.advance(n)
+        o.advance(n)
+    qt, q = inputs(rng, "fp8", (80, H, d))
+    out = g.attention(qt, 230, 2, 80, -0.5)
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 230, 2, 80, -0.5)
+    assert_attention_close(out, ref, "fp8")
+    ref2, _ = ring_attention(o, q, 230, 2, 80, -0.5)
+    assert_attention_close(out, ref2, "fp8")
+
+
 def test_attention_stream_full_size_sampled():
     banner("attention: streaming layer 757 x 5788 fp8, 40 heads, sampled rows")
     g, o, rng = stream_ring(WORKLOADS["stream"].seed)
