@@ -61,6 +61,7 @@ struct WriteArgs {
   int n_new, head, pos0, block_id;
   int lo_a, hi_a, lo_b, hi_b, chunks_a;
   int chunks, items;  // chunks per head group; chunks x head groups
+  int grid;           // workgroups launched (a multiple of 8)
   int use_rope;
   RopeTable rope;
 };
@@ -199,28 +200,35 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vt[kWHeads * D * RS];
 
   const int tid = threadIdx.x;
-  const int N = a.r.N, H = a.r.H;
+  // Every argument used before the first input load is read here in one
+  // batch of scalar loads; the empty asm keeps them from being spread over
+  // the dependent steps below (one argument round trip instead of several).
+  const int N = a.r.N, H = a.r.H, grid = a.grid, items = a.items, chunks = a.chunks;
+  const int chunks_a = a.chunks_a, lo_a = a.lo_a, hi_a = a.hi_a, lo_b = a.lo_b, hi_b = a.hi_b, head = a.head;
+  const void* const k_new = a.k_new;
+  const void* const v_new = a.v_new;
+  asm volatile("" ::"s"(N), "s"(H), "s"(grid), "s"(items), "s"(chunks), "s"(chunks_a), "s"(lo_a), "s"(hi_a),
+               "s"(lo_b), "s"(hi_b), "s"(head), "s"(k_new), "s"(v_new));
   // Workgroups are dealt to the 8 XCDs in turn; give each XCD a contiguous
   // range of work items, so that the neighbouring chunks whose V^T pieces
   // share 128-byte lines are written through the same L2.
-  const int per_xcd = gridDim.x / 8;
-  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (item >= a.items) return;
-  const int c = item % a.chunks;
-  const int group = item / a.chunks;
+  const int item = (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8;
+  if (item >= items) return;
+  const int c = item % chunks;
+  const int group = item / chunks;
   int base, lo, hi;
-  if (c < a.chunks_a) {
-    base = (a.lo_a / kWChunk + c) * kWChunk;
-    lo = max(base, a.lo_a);
-    hi = min(base + kWChunk, a.hi_a);
+  if (c < chunks_a) {
+    base = (lo_a / kWChunk + c) * kWChunk;
+    lo = max(base, lo_a);
+    hi = min(base + kWChunk, hi_a);
   } else {
-    base = (a.lo_b / kWChunk + (c - a.chunks_a)) * kWChunk;
-    lo = max(base, a.lo_b);
-    hi = min(base + kWChunk, a.hi_b);
+    base = (lo_b / kWChunk + (c - chunks_a)) * kWChunk;
+    lo = max(base, lo_b);
+    hi = min(base + kWChunk, hi_b);
   }
   // token index of slot s (slots of one chunk have consecutive tokens)
   auto token_of = [&](int s) {
-    int t = s - a.head;
+    int t = s - head;
     return t < 0 ? t + N : t;
   };
   const int piece = tid % kLanesPerRow;
@@ -238,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
     for (int w = 0; w < Raw<KV, EPL>::words; ++w) rk[i].w[w] = rv[i].w[w] = 0u;
     if (s >= lo && s < hi && h < H) {
       const size_t off = (static_cast<size_t>(token_of(s)) * H + h) * D + piece * EPL;
-      load_raw<KV, EPL>(a.k_new, off, rk[i]);
-      load_raw<KV, EPL>(a.v_new, off, rv[i]);
+      load_raw<KV, EPL>(k_new, off, rk[i]);
+      load_raw<KV, EPL>(v_new, off, rv[i]);
     }
   }
   double rev[EPL / 2];
@@ -453,8 +461,9 @@ hipError_t fill(void* p, size_t bytes, uint32_t value, hipStream_t s) {
 
 template <int KV, int D>
 hipError_t write_impl(const WriteArgs& a, hipStream_t s) {
-  const int grid = (a.items + 7) / 8 * 8;  // a multiple of 8 for the XCD mapping
-  hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(grid), dim3(kThreads), 0, s, a);
+  WriteArgs b = a;
+  b.grid = (a.items + 7) / 8 * 8;  // a multiple of 8 for the XCD mapping
+  hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(b.grid), dim3(kThreads), 0, s, b);
   return hipGetLastError();
 }
 

@@ -92,7 +92,8 @@ struct AttnArgs {
   float* part_o;    // [splits][n_q][H][d] when split
   float* part_lse;  // [splits][H][n_q]
   int n_qt, n_splits, tiles_per_split, n_tiles;
-  int remap;  // blockIdx -> work item remap keeps a head's tiles on one XCD
+  int remap;    // blockIdx -> work item remap keeps a head's tiles on one XCD
+  int n_items;  // workgroups launched
   int use_rope;
   RopeTable rope;
 };
@@ -336,6 +337,12 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float meta1[kHalves * KPS * kMetaWords];
   __shared__ float red[kWaves];
 
+  // Every argument used before the first loads is read here in one batch of
+  // scalar loads; the empty asm keeps them from being spread over the
+  // dependent steps below (one argument round trip instead of several).
+  asm volatile("" ::"s"(a.n_qt), "s"(a.n_splits), "s"(a.tiles_per_split), "s"(a.n_tiles), "s"(a.remap),
+               "s"(a.n_items), "s"(a.v_ld), "s"(a.H), "s"(a.n_q), "s"(a.k), "s"(a.v), "s"(a.q),
+               "s"(a.slot_block), "s"(a.k_scale), "s"(a.v_scale));
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: kept in SGPRs
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
 
   // ---- work item
   int item = blockIdx.x;
-  if (a.remap) item = (item % 8) * (gridDim.x / 8) + item / 8;
+  if (a.remap) item = (item % 8) * (a.n_items / 8) + item / 8;
   const int qt = item % a.n_qt;
   const int hs = item / a.n_qt;
   const int split = hs % a.n_splits;
@@ -920,6 +927,7 @@ hipError_t attn_impl(const RingView& r, const AttnCall& c, int splits, hipStream
   }
   const int total = a.n_qt * r.H * splits;
   a.remap = (total % 8 == 0) ? 1 : 0;
+  a.n_items = total;
   hipLaunchKernelGGL((chunk_attn_kernel<KV, D>), dim3(total), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
