@@ -646,10 +646,18 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
     // -- tile maximum of this query (both lane groups)
     float tmax;
     {
-      float m8[8];
+      // four independent chains of three-input maxima over 8 values each
+      float c4[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m8[e] = fmaxf(fmaxf(s[0][2 * e], s[0][2 * e + 1]), fmaxf(s[1][2 * e], s[1][2 * e + 1]));
-      tmax = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      for (int k = 0; k < 4; ++k) {
+        const v16f& v = s[k >> 1];
+        const int o = 8 * (k & 1);
+        float t = fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]);
+        t = fmaxf(fmaxf(t, v[o + 3]), v[o + 4]);
+        t = fmaxf(fmaxf(t, v[o + 5]), v[o + 6]);
+        c4[k] = fmaxf(t, v[o + 7]);
+      }
+      tmax = fmaxf(fmaxf(fmaxf(c4[0], c4[1]), c4[2]), c4[3]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
