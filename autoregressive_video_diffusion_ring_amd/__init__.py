@@ -105,7 +105,8 @@ class Ring:
     rc_ring struct the C ABI maintains."""
 
     def __init__(self, n_slots: int, n_heads: int, head_dim: int, kv_dtype: str = "fp8",
-                 rope_base: float = 10000.0, first_slot: int = 0, device="cuda", stream=None):
+                 rope_base: float = 10000.0, first_slot: int = 0, n_anchor: int = 0,
+                 device="cuda", stream=None):
         self.kv = DTYPES[kv_dtype]
         self.kv_name = kv_dtype
         self.device = torch.device(device)
@@ -118,6 +119,7 @@ class Ring:
         s.n_slots, s.n_heads, s.head_dim, s.kv_dtype = n_slots, n_heads, head_dim, self.kv
         s.rope_base = rope_base
         s.v_ld = rc_ring_v_ld(n_slots)
+        s.n_anchor = n_anchor
         s.k, s.v, s.k_scale, s.v_scale, s.slot_pos, s.slot_block = (_ptr(b) for b in self.buffers)
         rc_ring_init(s, first_slot, stream)
 
@@ -126,6 +128,7 @@ class Ring:
     H = property(lambda self: self.struct.n_heads)
     d = property(lambda self: self.struct.head_dim)
     v_ld = property(lambda self: self.struct.v_ld)
+    n_anchor = property(lambda self: self.struct.n_anchor)
     input_dtype = property(lambda self: _input_dtype(self.kv))
 
     def state(self) -> tuple[int, int, int, int, int]:

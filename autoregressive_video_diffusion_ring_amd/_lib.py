@@ -22,7 +22,7 @@ class RcRing(ctypes.Structure):
 
     _fields_ = [
         ("n_slots", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("kv_dtype", c_int32),
-        ("rope_base", c_float), ("v_ld", c_int32),
+        ("rope_base", c_float), ("v_ld", c_int32), ("n_anchor", c_int32),
         ("k", c_void_p), ("v", c_void_p), ("k_scale", c_void_p), ("v_scale", c_void_p),
         ("slot_pos", c_void_p), ("slot_block", c_void_p),
         ("head", c_int32), ("n_hist", c_int32), ("n_cur", c_int32), ("cur_pos0", c_int32),

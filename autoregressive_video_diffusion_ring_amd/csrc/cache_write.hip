@@ -7,9 +7,11 @@
 // byte of the cache written once, so both are organised to keep many loads
 // in flight: every thread issues all of its loads before any arithmetic.
 //
-// Write layout: the written range [head, head + n) mod N is cut into at most
-// two linear slot ranges, and each range into 32-slot chunks aligned to
-// multiples of 32.  One workgroup handles one chunk for kWHeads heads:
+// Write layout: the written range is cut into at most two linear slot
+// ranges, [head, min(head + n, N)) and the part past slot N-1, which wraps to
+// the first slot of the ring part (slot 0, or the first slot after the pinned
+// anchor slots), and each range into 32-slot chunks aligned to multiples of
+// 32.  One workgroup handles one chunk for kWHeads heads:
 //  * a row (one token of one head, d elements) is handled by 16 lanes with
 //    d/16 contiguous elements each, so a row's loads and stores are whole
 //    contiguous cache rows; a thread takes 4 consecutive slots of one head;
@@ -226,10 +228,12 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
     lo = max(base, lo_b);
     hi = min(base + kWChunk, hi_b);
   }
-  // token index of slot s (slots of one chunk have consecutive tokens)
+  // token index of slot s (slots of one chunk have consecutive tokens): slots
+  // from head on hold tokens 0.., the wrapped range [lo_b, hi_b) (below head)
+  // continues with token N - head
   auto token_of = [&](int s) {
     int t = s - head;
-    return t < 0 ? t + N : t;
+    return t < 0 ? t + (N - lo_b) : t;
   };
   const int piece = tid % kLanesPerRow;
   const int rg = tid / kLanesPerRow;
@@ -505,10 +509,11 @@ hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* 
   a.block_id = block_id;
   a.lo_a = head;
   a.hi_a = std::min(head + n_new, r.N);
-  a.lo_b = 0;
-  a.hi_b = head + n_new > r.N ? head + n_new - r.N : 0;
+  // the part past slot N-1 wraps to the first slot of the ring part
+  a.lo_b = r.n_anchor;
+  a.hi_b = head + n_new > r.N ? r.n_anchor + head + n_new - r.N : r.n_anchor;
   a.chunks_a = (a.hi_a - 1) / kWChunk - a.lo_a / kWChunk + 1;
-  const int chunks_b = a.hi_b > 0 ? (a.hi_b - 1) / kWChunk + 1 : 0;
+  const int chunks_b = a.hi_b > a.lo_b ? (a.hi_b - 1) / kWChunk - a.lo_b / kWChunk + 1 : 0;
   a.use_rope = r.rope_base > 0.f;
   a.rope = make_rope(r.rope_base, r.d);
   a.chunks = a.chunks_a + chunks_b;

@@ -8,12 +8,18 @@
 // min(n_hist, N - n).  The chunk stays "current" (n_cur = n) through its
 // denoising passes, each of which writes the same slots again, until
 // rc_ring_advance commits it: head += n (mod N), n_hist += n, n_cur = 0.
+// With an anchor of A slots the ring part is slots A..N-1: every wrap goes
+// from N back to A, so the first A tokens of the stream stay in slots 0..A-1
+// (the anchor starts filling at slot 0), and a chunk holds at most N - A
+// tokens.  n_hist keeps the same update rules: a write evicts the oldest
+// tokens of the ring part only.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +27,10 @@
 
 #include "../../include/rc.h"
 #include "rc_kernels.h"
+
+// The layout the Python binding mirrors.
+static_assert(offsetof(rc_ring, n_anchor) == 24 && offsetof(rc_ring, k) == 32, "rc_ring layout");
+static_assert(offsetof(rc_ring, head) == 80 && sizeof(rc_ring) == 104, "rc_ring layout");
 
 namespace {
 
@@ -66,6 +76,8 @@ rc_status check_ring(const rc_ring* r) {
   if (r->v_ld != rc_ring_v_ld(r->n_slots))
     return fail(RC_ERR_ARG, "v_ld must be rc_ring_v_ld(n_slots) = %d (got %d)", rc_ring_v_ld(r->n_slots), r->v_ld);
   if (!std::isfinite(r->rope_base) || r->rope_base < 0.f) return fail(RC_ERR_ARG, "rope_base must be >= 0");
+  if (r->n_anchor < 0 || r->n_anchor >= r->n_slots)
+    return fail(RC_ERR_ARG, "n_anchor must be in 0..%d (got %d)", r->n_slots - 1, r->n_anchor);
   if (!r->k || !r->v || !r->slot_pos || !r->slot_block) return fail(RC_ERR_ARG, "ring device pointer is NULL");
   if (r->kv_dtype == RC_FP8_E4M3 && (!r->k_scale || !r->v_scale))
     return fail(RC_ERR_ARG, "FP8 ring needs k_scale and v_scale");
@@ -89,6 +101,7 @@ rc::RingView view(const rc_ring* r) {
   v.d = r->head_dim;
   v.kv = r->kv_dtype;
   v.v_ld = r->v_ld;
+  v.n_anchor = r->n_anchor;
   v.rope_base = r->rope_base;
   v.k = r->k;
   v.v = r->v;
@@ -100,6 +113,13 @@ rc::RingView view(const rc_ring* r) {
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// The slot n places after `head`, wrapping from N to the ring part's first
+// slot (n_anchor); n <= N - n_anchor.
+int32_t step_slot(const rc_ring* r, int32_t head, int32_t n) {
+  const int32_t s = head + n;
+  return s < r->n_slots ? s : s - r->n_slots + r->n_anchor;
+}
 
 }  // namespace
 
@@ -128,6 +148,8 @@ rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
   if (st != RC_OK) return st;
   if (first_slot < 0 || first_slot >= r->n_slots)
     return fail(RC_ERR_ARG, "first_slot must be in 0..%d (got %d)", r->n_slots - 1, first_slot);
+  if (r->n_anchor > 0 && first_slot != 0)
+    return fail(RC_ERR_ARG, "a ring with an anchor starts at slot 0 (got first_slot %d)", first_slot);
   hipError_t e = rc::launch_ring_clear(view(r), as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "ring clear");
   r->head = first_slot;
@@ -146,8 +168,8 @@ rc_status rc_cache_write(rc_ring* r, const void* k_new, const void* v_new, int32
   if (!k_new || !v_new) return fail(RC_ERR_ARG, "k_new / v_new is NULL");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
     return fail(RC_ERR_ARG, "k_new and v_new must be 16-byte aligned");
-  if (n_new < 1 || n_new > r->n_slots)
-    return fail(RC_ERR_ARG, "n_new must be in 1..%d (got %d)", r->n_slots, n_new);
+  if (n_new < 1 || n_new > r->n_slots - r->n_anchor)
+    return fail(RC_ERR_ARG, "n_new must be in 1..%d (N - n_anchor; got %d)", r->n_slots - r->n_anchor, n_new);
   if (block_id < 0) return fail(RC_ERR_ARG, "block_id must be >= 0 (got %d)", block_id);
   if (static_cast<long long>(pos0) + n_new - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
   if (r->n_cur > 0 && (n_new != r->n_cur || pos0 != r->cur_pos0 || block_id != r->cur_block))
@@ -209,11 +231,13 @@ rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32
 
 rc_status rc_ring_advance(rc_ring* r, int32_t n) {
   if (!r) return fail(RC_ERR_ARG, "ring is NULL");
+  if (r->n_slots < 1 || r->n_anchor < 0 || r->n_anchor >= r->n_slots)
+    return fail(RC_ERR_ARG, "bad n_slots / n_anchor (%d / %d)", r->n_slots, r->n_anchor);
   rc_status st = check_state(r);
   if (st != RC_OK) return st;
   if (r->n_cur == 0 || n != r->n_cur)
     return fail(RC_ERR_STATE, "advance(%d) needs n == n_cur > 0 (n_cur %d)", n, r->n_cur);
-  r->head = (r->head + n) % r->n_slots;
+  r->head = step_slot(r, r->head, n);
   r->n_hist = std::min(r->n_hist + n, r->n_slots);
   r->n_cur = 0;
   return ok();

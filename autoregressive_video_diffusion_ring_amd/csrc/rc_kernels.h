@@ -11,6 +11,7 @@ namespace rc {
 struct RingView {
   int N, H, d, kv, v_ld;
   float rope_base;
+  int n_anchor;  // slots 0..n_anchor-1 are pinned; writes wrap from N to n_anchor
   void* k;
   void* v;
   float* k_scale;
@@ -23,7 +24,8 @@ enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 hipError_t launch_ring_clear(const RingView& r, hipStream_t s);
 
-// Writes n_new tokens to slots (head + i) mod N.
+// Writes n_new tokens to slots head + i, wrapping from N to n_anchor
+// (n_new <= N - n_anchor).
 hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* v_new, int n_new,
                               int head, int pos0, int block_id, hipStream_t s);
 

@@ -27,7 +27,8 @@ ten blocks' queries.
 ``--longrun K`` instead runs K chunks of the long-run schedule (a position
 reset every 300 chunks by a delta rotation of all 60 rings, ten cache-bias
 ramps 0, -2, -4, -2, 0) and prints one JSON line with the sustained ms/chunk
-(median and p99).
+(median and p99).  ``--anchor A`` makes those rings anchored: the first A
+tokens (A = 757: the first chunk) stay pinned and the other slots slide.
 """
 from __future__ import annotations
 
@@ -182,11 +183,14 @@ def bias_at(t: int) -> float:
     return 0.0
 
 
-def longrun(n_chunks: int) -> dict:
+def longrun(n_chunks: int, anchor: int = 0) -> dict:
     """Sustained chunks of the long-run schedule from an empty cache: each
     chunk is 4 passes x 60 layers of write + attention, then 60 advances;
-    before every 300th chunk all 60 rings are rerotated so that the oldest
-    cached position becomes 0; the cache bias follows ten ramps."""
+    before every 300th chunk all 60 rings are rerotated so that the most
+    recent N cached positions become 0..N-1 (the oldest cached position of a
+    plain ring; an anchor, older still, moves below 0 with them); the cache
+    bias follows ten ramps.  With anchor > 0 every ring pins its first
+    `anchor` tokens."""
     import torch
 
     from autoregressive_video_diffusion_ring_amd import Ring, rc_cache_write, rc_chunk_attention, rc_ring_advance
@@ -195,7 +199,7 @@ def longrun(n_chunks: int) -> dict:
     sptr = stream.cuda_stream
     gen = torch.Generator(device=dev)
     gen.manual_seed(4)
-    rings = [Ring(N, H, D, "fp8", 10000.0, device=dev) for _ in range(LAYERS)]
+    rings = [Ring(N, H, D, "fp8", 10000.0, n_anchor=anchor, device=dev) for _ in range(LAYERS)]
     pool = [[torch.randn((NEW, H, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
              for _ in range(3)] for _ in range(POOL)]
     out = torch.empty((NEW, H, D), dtype=torch.bfloat16, device=dev)
@@ -228,8 +232,10 @@ def longrun(n_chunks: int) -> dict:
     steady = sorted(m for i, m in enumerate(ms) if i >= 8 and i not in resets)
     full = sorted(ms[8:])
     pick = lambda v, f: v[min(len(v) - 1, int(f * len(v)))]
-    return {"metric": "sustained ms/chunk, long-run schedule (757 new x 5788-slot fp8 ring, 60 layers)",
+    kind = f"anchored fp8 ring, first {anchor} tokens pinned" if anchor else "fp8 ring"
+    return {"metric": f"sustained ms/chunk, long-run schedule (757 new x 5788-slot {kind}, 60 layers)",
             "value": round(pick(full, 0.5), 4), "unit": "ms", "higher_is_better": False,
+            "n_anchor": anchor, "final_head": rings[0].state()[0],
             "chunks": n_chunks, "p99_ms": round(pick(full, 0.99), 4), "mean_ms": round(sum(full) / len(full), 4),
             "steady_median_ms": round(pick(steady, 0.5), 4),
             "reset_chunk_ms": [round(ms[i], 3) for i in resets],
@@ -271,6 +277,8 @@ def main() -> int:
     ap.add_argument("--no-joint-av", action="store_true", help="skip the joint audio-video paths")
     ap.add_argument("--longrun", type=int, default=0, metavar="K",
                     help="run K chunks of the long-run schedule instead and print that line")
+    ap.add_argument("--anchor", type=int, default=0, metavar="A",
+                    help="with --longrun: pin the first A tokens of every ring (757 = the first chunk)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,7 +293,7 @@ def main() -> int:
 
     if args.longrun > 0:
         torch.cuda.set_device(0)
-        print(json.dumps(longrun(args.longrun)), flush=True)
+        print(json.dumps(longrun(args.longrun, args.anchor)), flush=True)
         return 0
 
     dev = torch.device("cuda", 0)

@@ -65,6 +65,15 @@ typedef enum {
  *   slot_block [v_ld]   int32   block id of each slot, -1 = never written
  * Entries s in [N, v_ld) are padding: the kernels read them as empty slots
  * (block -1, scale 0, V 0) and never write them.
+ * Anchor + sliding window (Why Live Video Generation Still Struggles With
+ * Timing, transcript: the first chunk kept as a permanent anchor beside recent
+ * history; StreamLTX project page, "Why a long take does not slow down": an
+ * anchor next to a FIFO).  With n_anchor = A > 0 the first A tokens written
+ * fill slots 0..A-1 and are never evicted; every later token goes to the
+ * sliding part, slots A..N-1, used as a ring of N - A slots.  Writes then wrap
+ * from slot N-1 to slot A instead of slot 0.  An anchored ring starts at slot 0
+ * and its chunks hold at most N - A tokens.  Attention and re-rotation treat
+ * anchor slots like any other written slot.
  * Host state (maintained by the library; read it, do not write it):
  *   head       next slot to write
  *   n_hist     committed history tokens in the cache
@@ -78,6 +87,7 @@ typedef struct rc_ring {
   int32_t kv_dtype;    /* rc_dtype */
   float rope_base;     /* RoPE base (10000 on the pages' workloads); 0 = no RoPE */
   int32_t v_ld;        /* must equal rc_ring_v_ld(n_slots) */
+  int32_t n_anchor;    /* A pinned slots, 0 <= A < N (0 = plain ring); see below */
   void* k;
   void* v;
   float* k_scale;
@@ -101,13 +111,15 @@ rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int3
 /*
  * Validate the geometry and pointers, zero K, V and the scales, set every
  * slot_block to -1 and slot_pos to 0 (asynchronously on `stream`), and set the
- * host state: head = first_slot (0 <= first_slot < N), n_hist = n_cur = 0.
+ * host state: head = first_slot (0 <= first_slot < N; 0 when n_anchor > 0),
+ * n_hist = n_cur = 0.
  */
 rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
 
 /*
- * Write n_new tokens into slots (head + i) mod N, i < n_new (Runway
- * Characters, abstract: ring cache, RoPE and FP8 quantisation once per write).
+ * Write n_new tokens into slots head + i, i < n_new, wrapping from N to
+ * n_anchor (so (head + i) mod N without an anchor) (Runway Characters,
+ * abstract: ring cache, RoPE and FP8 quantisation once per write).
  *   k_new, v_new  device [n_new][H][d], bfloat16 (float32 for an RC_F32 ring),
  *                 token-major as a QKV projection produces them
  *   pos0          position of token 0; token i has position pos0 + i
@@ -119,7 +131,7 @@ rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
  * History slots overwritten by the write are evicted: n_hist becomes
  * min(n_hist, N - n_new).  Every denoising pass of one chunk writes again
  * before rc_ring_advance: while n_cur > 0, n_new, pos0 and block_id must repeat
- * the current chunk's, else RC_ERR_STATE.  Requires 1 <= n_new <= N.
+ * the current chunk's, else RC_ERR_STATE.  Requires 1 <= n_new <= N - n_anchor.
  */
 rc_status rc_cache_write(rc_ring* ring, const void* k_new, const void* v_new, int32_t n_new,
                          int32_t pos0, int32_t block_id, void* stream);
@@ -165,7 +177,8 @@ size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
 
 /*
  * Commit the current chunk as history (host only, nothing is enqueued):
- * head = (head + n) mod N, n_hist += n, n_cur = 0.  Requires n == n_cur > 0.
+ * head moves n slots on (wrapping from N to n_anchor), n_hist =
+ * min(n_hist + n, N), n_cur = 0.  Requires n == n_cur > 0.
  */
 rc_status rc_ring_advance(rc_ring* ring, int32_t n);
 

@@ -20,6 +20,22 @@ bookkeeping below is the plainest reading of "ring cache":
 * ``rerotate(delta)``: every written slot's key is dequantised, rotated by
   delta and quantised again; its position moves by delta; V is untouched.
 
+Anchor + sliding window ("Why Live Video Generation Still Struggles With
+Timing", transcript: a streaming editor keeps the first chunk as a permanent
+anchor beside a window of recent history; StreamLTX project page, "Why a long
+take does not slow down": an anchor next to a FIFO of recent blocks).
+Plainest reading, with A = n_anchor pinned slots (0 = the plain ring):
+
+* the first A tokens ever written fill slots 0..A-1 and stay there;
+* every later token goes to the sliding part, slots A..N-1, as a ring of
+  N - A slots: token k of the stream (k >= A; the passes of one chunk
+  rewrite the same tokens) lands in slot A + (k - A) mod (N - A).
+In head terms: a write of n tokens goes to head + i while that is below N
+and wraps to A + (head + i - N); a chunk must fit the sliding part
+(n <= N - A), so a write never covers an anchor slot once they are filled.
+An anchored ring starts at slot 0.  n_hist keeps its meaning (committed
+tokens in the cache, anchor included) and its update rules.
+
 Storage per layer, logical layout [H][N][d]:
 * fp8:  K and V as e4m3fn codes plus float32 scales [H][N];
 * bf16: K and V rounded to bfloat16 (nearest, ties to even);
@@ -62,14 +78,19 @@ class Ring:
     """One layer's ring cache plus its host state."""
 
     def __init__(self, n_slots: int, n_heads: int, head_dim: int, kv_dtype: str,
-                 rope_base: float, first_slot: int = 0):
+                 rope_base: float, first_slot: int = 0, n_anchor: int = 0):
         if kv_dtype not in ("fp8", "bf16", "f32"):
             raise ValueError(kv_dtype)
         if n_slots < 1 or n_heads < 1 or head_dim < 2 or head_dim % 2:
             raise ValueError("bad ring shape")
         if not 0 <= first_slot < n_slots:
             raise ValueError("first_slot out of range")
+        if not 0 <= n_anchor < n_slots:
+            raise ValueError("n_anchor must be in 0..N-1")
+        if n_anchor > 0 and first_slot != 0:
+            raise ValueError("an anchored ring starts at slot 0")
         self.N, self.H, self.d = n_slots, n_heads, head_dim
+        self.A = n_anchor
         self.kv_dtype = kv_dtype
         self.rope_base = float(rope_base)
         shape = (n_heads, n_slots, head_dim)
@@ -106,9 +127,16 @@ class Ring:
             return e4m3.dequantize(self.v, self.v_scale)
         return self.v.copy()
 
+    def _step(self, i):
+        """Slot i places after head, wrapping from N back to the first
+        slot of the sliding part (slot A; slot 0 without an anchor)."""
+        s = self.head + np.asarray(i)
+        return np.where(s < self.N, s, s - self.N + self.A)
+
     def write_slots(self, n: int) -> np.ndarray:
-        """Slots a write of n tokens goes to: (head + i) mod N."""
-        return (self.head + np.arange(n)) % self.N
+        """Slots a write of n tokens goes to: head + i, wrapped into A..N-1
+        ((head + i) mod N without an anchor)."""
+        return self._step(np.arange(n))
 
     # ------------------------------------------------------------- writes
     def _encode_into(self, dst, dst_scale, slots, x_hnd):
@@ -123,8 +151,8 @@ class Ring:
     def write(self, k_new: np.ndarray, v_new: np.ndarray, n: int, pos0: int,
               block_id: int) -> None:
         """Write n new tokens; k_new and v_new are float64 [n][H][d]."""
-        if not 1 <= n <= self.N:
-            raise ValueError("n_new must be in 1..N")
+        if not 1 <= n <= self.N - self.A:
+            raise ValueError("n_new must be in 1..N - n_anchor")
         if block_id < 0:
             raise ValueError("block_id must be >= 0")
         k_new = np.asarray(k_new, dtype=np.float64)
@@ -160,17 +188,17 @@ class Ring:
         """Commit the current chunk of n tokens as history."""
         if self.n_cur == 0 or n != self.n_cur:
             raise RingStateError("advance(n) needs n == n_cur > 0")
-        self.head = (self.head + n) % self.N
+        self.head = int(self._step(n))
         self.n_hist = min(self.n_hist + n, self.N)
         self.n_cur = 0
 
     # ---------------------------------------------------------- transport
     @classmethod
     def from_arrays(cls, *, kv_dtype, rope_base, k, v, k_scale, v_scale, slot_pos,
-                    slot_block, state=(0, 0, 0, 0, 0)):
+                    slot_block, state=(0, 0, 0, 0, 0), n_anchor=0):
         """Build a ring from given cache contents (logical layout [H][N][d])."""
         H, N, d = k.shape
-        r = cls(N, H, d, kv_dtype, rope_base)
+        r = cls(N, H, d, kv_dtype, rope_base, n_anchor=n_anchor)
         if kv_dtype == "fp8":
             r.k = np.array(k, dtype=np.uint8)
             r.v = np.array(v, dtype=np.uint8)

@@ -38,18 +38,20 @@ def test_library_exports_every_header_symbol():
 
 
 def test_struct_layout_matches_c():
-    # int32 x 5, float, int32, then six pointers at 8-byte alignment, then 5 int32
-    assert RcRing.k.offset == 24 and RcRing.slot_block.offset == 64
-    assert RcRing.head.offset == 72 and RcRing.cur_block.offset == 88
-    assert ctypes.sizeof(RcRing) == 96
+    # int32 x 4, float, int32 x 2, then six pointers at 8-byte alignment, then 5 int32
+    assert RcRing.n_anchor.offset == 24
+    assert RcRing.k.offset == 32 and RcRing.slot_block.offset == 72
+    assert RcRing.head.offset == 80 and RcRing.cur_block.offset == 96
+    assert ctypes.sizeof(RcRing) == 104
 
 
 FAKE = 1 << 20  # aligned placeholder address; never dereferenced by the checks below
 
 
-def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0):
+def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0, n_anchor=0):
     r = RcRing()
     r.n_slots, r.n_heads, r.head_dim, r.kv_dtype = N, H, d, kv
+    r.n_anchor = n_anchor
     r.rope_base = 10000.0
     r.v_ld = lib().rc_ring_v_ld(N)
     r.k = r.v = r.k_scale = r.v_scale = r.slot_pos = r.slot_block = FAKE
@@ -74,16 +76,19 @@ def test_v_ld_and_sizes():
     assert L.rc_ring_sizes(10, 2, 64, 7, out) == RC_ERR_ARG
 
 
-@pytest.mark.parametrize("N,n,h0,chunks", [(5788, 757, 5031, 30), (96, 32, 0, 9), (10, 10, 3, 4), (7, 3, 6, 12)])
-def test_advance_matches_oracle(N, n, h0, chunks):
-    """Host bookkeeping of write + advance, bit-exact against the oracle.
+@pytest.mark.parametrize("N,n,h0,chunks,A", [(5788, 757, 5031, 30, 0), (96, 32, 0, 9, 0), (10, 10, 3, 4, 0),
+                                             (7, 3, 6, 12, 0), (5788, 757, 0, 30, 757), (10, 3, 0, 12, 3),
+                                             (10, 3, 0, 12, 4), (7, 1, 0, 20, 6)])
+def test_advance_matches_oracle(N, n, h0, chunks, A):
+    """Host bookkeeping of write + advance, bit-exact against the oracle,
+    with and without pinned anchor slots.
 
     The write's device work cannot run here, so the write's host update is
     replayed by hand exactly as rc_cache_write applies it after a successful
     launch; rc_ring_advance itself runs in the library."""
     L = lib()
-    r = fake_ring(N, head=h0)
-    o = OracleRing(N, 1, 2, "f32", 0.0, first_slot=h0)
+    r = fake_ring(N, head=h0, n_anchor=A)
+    o = OracleRing(N, 1, 2, "f32", 0.0, first_slot=h0, n_anchor=A)
     z = np.zeros((n, 1, 2))
     for t in range(chunks):
         o.write(z, z, n, n * t, t)
@@ -128,6 +133,14 @@ def test_write_argument_and_state_checks():
         got = L.rc_cache_write(ctypes.byref(r), k, v, n, pos0, blk, None)
         assert got == want, (n, pos0, blk, got, L.rc_last_error())
         assert state(r) == before
+    ra = fake_ring(100, n_anchor=30)
+    assert L.rc_cache_write(ctypes.byref(ra), FAKE, FAKE, 71, 0, 0, None) == RC_ERR_ARG  # > N - n_anchor
+    assert "n_anchor" in L.rc_last_error().decode()
+    ra.n_anchor = 100
+    assert L.rc_cache_write(ctypes.byref(ra), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
+    ra.n_anchor = -1
+    assert L.rc_cache_write(ctypes.byref(ra), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
+    assert state(ra) == (0, 0, 0, 0, 0)
     r2 = fake_ring(100)
     r2.v_ld = 100  # wrong leading dimension
     assert L.rc_cache_write(ctypes.byref(r2), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
@@ -176,3 +189,17 @@ def test_init_checks():
     assert L.rc_ring_init(ctypes.byref(r), -1, None) == RC_ERR_ARG
     r.slot_block = 0
     assert L.rc_ring_init(ctypes.byref(r), 0, None) == RC_ERR_ARG
+    a = fake_ring(100, n_anchor=20)
+    assert L.rc_ring_init(ctypes.byref(a), 5, None) == RC_ERR_ARG   # an anchored ring starts at 0
+    a.n_anchor = 100
+    assert L.rc_ring_init(ctypes.byref(a), 0, None) == RC_ERR_ARG
+
+
+def test_advance_checks_anchor():
+    L = lib()
+    r = fake_ring(10, n_anchor=10, n_cur=3)
+    assert L.rc_ring_advance(ctypes.byref(r), 3) == RC_ERR_ARG
+    r.n_anchor = 3
+    r.head = 9
+    assert L.rc_ring_advance(ctypes.byref(r), 3) == RC_OK
+    assert state(r)[:3] == (5, 3, 0)    # 9 -> 3 + (9 + 3 - 10)

@@ -38,9 +38,9 @@ def banner(msg):
     sys.stdout.flush()
 
 
-def make_pair(N, H, d, kv, rope, first_slot=0):
-    return (Ring(N, H, d, kv, rope, first_slot=first_slot, device=DEV),
-            OracleRing(N, H, d, kv, rope, first_slot=first_slot))
+def make_pair(N, H, d, kv, rope, first_slot=0, n_anchor=0):
+    return (Ring(N, H, d, kv, rope, first_slot=first_slot, n_anchor=n_anchor, device=DEV),
+            OracleRing(N, H, d, kv, rope, first_slot=first_slot, n_anchor=n_anchor))
 
 
 def write_both(g, o, rng, n, pos0, blk):
@@ -123,6 +123,46 @@ def test_write_other_formats(kv, d):
     o.advance(77)
     write_both(g, o, rng, 150, 1077, 1)
     compare_cache(gpu_cache(g), o, kv)
+
+
+@pytest.mark.parametrize("kv,d,N,A,n,H,chunks", [
+    ("fp8", 128, 300, 50, 77, 3, 9),       # chunk 0 straddles the anchor; ragged wraps to slot 50
+    ("bf16", 64, 200, 64, 40, 3, 10),
+    ("fp8", 128, 5788, 757, 757, 8, 9),    # the streaming shape with the first chunk pinned
+])
+def test_anchor_ring_stream(kv, d, N, A, n, H, chunks):
+    """Anchor + sliding window: the first A tokens stay pinned in slots 0..A-1
+    while the ring part A..N-1 wraps.  Cache contents and bookkeeping after
+    every write (and a second pass over a wrapping chunk), then a position
+    reset, then block-causal attention over the whole cache."""
+    banner(f"anchor ring: {kv} d={d} N={N} A={A} chunks of {n}, H={H}, {chunks} chunks")
+    rng = np.random.default_rng(41)
+    g, o = make_pair(N, H, d, kv, 10000.0, n_anchor=A)
+    wrapped = False
+    for b in range(chunks):
+        write_both(g, o, rng, n, n * b, b)
+        compare_cache(gpu_cache(g), o, kv)
+        if g.state()[0] + n > N:   # this chunk wraps: a second pass must hit the same slots
+            wrapped = True
+            write_both(g, o, rng, n, n * b, b)
+            compare_cache(gpu_cache(g), o, kv)
+        if b + 1 < chunks:
+            g.advance(n)
+            o.advance(n)
+    assert wrapped
+    c = gpu_cache(g)   # the anchor still holds the first A tokens of the stream
+    assert np.array_equal(c["slot_pos"][:A], np.arange(A))
+    assert np.array_equal(c["slot_block"][:A], np.arange(A) // n)
+    g.rerotate(-1000)
+    o.rerotate(-1000)
+    c = gpu_cache(g)
+    assert np.array_equal(c["slot_pos"][:A], np.arange(A) - 1000)
+    q_pos0, q_blk = n * (chunks - 1) - 1000, chunks - 1
+    qt, q = inputs(rng, kv, (n, H, d))
+    out = g.attention(qt, q_pos0, q_blk, n, -0.5)
+    rows = np.r_[0:n:max(1, n // 60), n - 3:n]
+    ref, _ = oracle_rows(oracle_from_gpu(g, 10000.0), q, rows, q_pos0, q_blk, n, -0.5)
+    assert_attention_close(out, ref, kv, rows=rows)
 
 
 # ------------------------------------------------------------------ rerotate

@@ -2,7 +2,9 @@
 
 * Bookkeeping is checked against an independent model (a replay of every
   token ever written into explicit cells, the k-th token going to cell
-  (first + k) mod N) under random call sequences drawn by Hypothesis.
+  (first + k) mod N, or with an anchor of A slots to cell k for k < A and
+  A + (k - A) mod (N - A) after) under random call sequences drawn by
+  Hypothesis.
 * Closed forms: the head after T chunks of n tokens is (h0 + n T) mod N.
 * Write: cached values are the rotated inputs up to one quantisation step.
 * Delta rotation equals re-encoding at the moved positions: exactly up to
@@ -21,8 +23,8 @@ class CellModel:
     """Independent model: a list of all tokens written (the current chunk can
     be rewritten), replayed into N cells."""
 
-    def __init__(self, N, first):
-        self.N, self.first = N, first
+    def __init__(self, N, first, A=0):
+        self.N, self.first, self.A = N, first, A
         self.committed = []  # (pos, block)
         self.current = []
 
@@ -37,11 +39,16 @@ class CellModel:
         self.committed += self.current
         self.current = []
 
+    def cell(self, k):
+        if k < self.A:
+            return k
+        return self.A + (self.first + k - self.A) % (self.N - self.A)
+
     def cells(self):
         pos = {}
         owner = {}
         for k, tok in enumerate(self.committed + self.current):
-            c = (self.first + k) % self.N
+            c = self.cell(k)
             pos[c] = tok
             owner[c] = k
         return pos, owner
@@ -49,7 +56,7 @@ class CellModel:
     def expect(self):
         pos, owner = self.cells()
         nc = len(self.committed)
-        head = (self.first + nc) % self.N
+        head = self.cell(nc)
         n_hist = sum(1 for c, k in owner.items() if k < nc)
         slot_pos = np.zeros(self.N, dtype=np.int64)
         slot_block = np.full(self.N, -1, dtype=np.int64)
@@ -63,15 +70,17 @@ ops = st.lists(st.tuples(st.sampled_from(["write", "advance", "rerotate", "rewri
 
 
 @settings(max_examples=300, deadline=None)
-@given(N=st.integers(1, 40), first=st.integers(0, 39), seq=ops)
-def test_bookkeeping_matches_cell_model(N, first, seq):
-    first %= N
+@given(N=st.integers(1, 40), first=st.integers(0, 39), anchor=st.integers(0, 39), seq=ops)
+def test_bookkeeping_matches_cell_model(N, first, anchor, seq):
+    # half the cases without an anchor (any first slot), half with one
+    A = 0 if anchor % 2 == 0 else (anchor // 2) % N
+    first = first % N if A == 0 else 0
     H, d = 1, 2
-    ring = Ring(N, H, d, "f32", 0.0, first_slot=first)
-    model = CellModel(N, first)
+    ring = Ring(N, H, d, "f32", 0.0, first_slot=first, n_anchor=A)
+    model = CellModel(N, first, A)
     pos_next, blk_next = 0, 0
     for op, n, delta in seq:
-        n = (n - 1) % N + 1
+        n = (n - 1) % (N - A) + 1
         if op == "write" and ring.n_cur == 0:
             z = np.zeros((n, H, d))
             ring.write(z, z, n, pos_next, blk_next)
@@ -145,6 +154,77 @@ def test_wrap_and_eviction_slots():
     assert np.array_equal(np.nonzero(ring2.slot_block == 0)[0], np.r_[0:16, 80:96])
     assert np.array_equal(ring2.slot_pos[80:96], np.arange(16))
     assert np.array_equal(ring2.slot_pos[0:16], np.arange(16, 32))
+
+
+def test_anchor_slots_by_hand():
+    """Anchor of 3 slots in a 10-slot ring, chunks of 3 tokens (chunk b has
+    positions 3b..3b+2): slots 0..2 keep chunk 0, the sliding part 3..9
+    wraps back to slot 3.  Expected contents derived by hand:
+    chunk 1 -> 3,4,5; chunk 2 -> 6,7,8; chunk 3 -> 9,3,4; chunk 4 -> 5,6,7;
+    chunk 5 -> 8,9,3."""
+    N, A, n = 10, 3, 3
+    ring = Ring(N, 1, 2, "f32", 0.0, n_anchor=A)
+    z = np.zeros((n, 1, 2))
+    heads = []
+    for b in range(6):
+        ring.write(z, z, n, 3 * b, b)
+        ring.advance(n)
+        heads.append(ring.head)
+    assert heads == [3, 6, 9, 5, 8, 4]
+    assert ring.n_hist == 10
+    assert ring.slot_block.tolist() == [0, 0, 0, 5, 3, 4, 4, 4, 5, 5]
+    assert ring.slot_pos.tolist() == [0, 1, 2, 17, 11, 12, 13, 14, 15, 16]
+    # the next write evicts the two oldest sliding tokens (slots 4, 5), never the anchor
+    ring.write(z[:2], z[:2], 2, 18, 6)
+    assert ring.write_slots(2).tolist() == [4, 5] and ring.n_hist == 8
+    assert ring.slot_block.tolist() == [0, 0, 0, 5, 6, 6, 4, 4, 5, 5]
+
+
+def test_anchor_filled_by_a_straddling_chunk():
+    """Anchor of 4 slots, chunks of 3: chunk 1 puts one token in the anchor
+    and two in the sliding part; the wrap then returns to slot 4."""
+    N, A, n = 10, 4, 3
+    ring = Ring(N, 1, 2, "f32", 0.0, n_anchor=A)
+    z = np.zeros((n, 1, 2))
+    for b in range(4):
+        ring.write(z, z, n, 3 * b, b)
+        ring.advance(n)
+    assert ring.head == 6
+    assert ring.slot_block.tolist() == [0, 0, 0, 1, 3, 3, 2, 2, 2, 3]
+    assert ring.slot_pos.tolist() == [0, 1, 2, 3, 10, 11, 6, 7, 8, 9]
+
+
+def test_anchor_keeps_first_chunk_over_a_long_take():
+    """The pages' shape: 5788 slots, chunks of 757 tokens, the first chunk
+    pinned.  After every chunk the anchor still holds chunk 0 (positions
+    0..756) and the sliding part holds the most recent 5031 tokens."""
+    N, n = 5788, 757
+    A = n
+    ring = Ring(N, 1, 2, "f32", 0.0, n_anchor=A)
+    z = np.zeros((n, 1, 2))
+    for T in range(1, 30):
+        ring.write(z, z, n, n * (T - 1), T - 1)
+        ring.advance(n)
+        assert np.all(ring.slot_block[:A] == 0)
+        assert np.array_equal(ring.slot_pos[:A], np.arange(A))
+        total = n * T
+        recent = np.arange(max(A, total - (N - A)), total)  # token index = position
+        held = np.sort(ring.slot_pos[A:][ring.slot_block[A:] != -1])
+        assert np.array_equal(held, recent)
+        assert ring.n_hist == min(total, N)
+
+
+def test_anchor_argument_checks():
+    with pytest.raises(ValueError):
+        Ring(10, 1, 2, "f32", 0.0, n_anchor=10)
+    with pytest.raises(ValueError):
+        Ring(10, 1, 2, "f32", 0.0, n_anchor=-1)
+    with pytest.raises(ValueError):
+        Ring(10, 1, 2, "f32", 0.0, first_slot=2, n_anchor=3)
+    ring = Ring(10, 1, 2, "f32", 0.0, n_anchor=3)
+    with pytest.raises(ValueError):   # a chunk must fit the sliding part
+        ring.write(np.zeros((8, 1, 2)), np.zeros((8, 1, 2)), 8, 0, 0)
+    assert ring.state() == (0, 0, 0, 0, 0)
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16", "f32"])
