@@ -5,7 +5,9 @@ only for device memory and streams; every step of the path runs in the HIP
 kernels behind the C ABI.  The entry points keep the C names:
 
     rc_ring_init, rc_cache_write, rc_cache_rerotate, rc_chunk_attention,
-    rc_ring_advance, rc_attention_workspace_bytes, rc_debug_visibility
+    rc_ring_advance, rc_attention_workspace_bytes, rc_debug_visibility,
+    rc_key_mass, rc_key_mass_workspace_bytes, rc_cache_write_scored,
+    rc_cache_write_scored_workspace_bytes
 
 and ``Ring`` owns a ring's device buffers (torch tensors) and its rc_ring
 struct.  See include/rc.h for the meaning of every argument.
@@ -21,7 +23,8 @@ from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RcError, RcRing, check,
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
-    "rc_ring_sizes", "rc_ring_v_ld",
+    "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_workspace_bytes", "rc_cache_write_scored",
+    "rc_cache_write_scored_workspace_bytes",
 ]
 
 
@@ -94,6 +97,28 @@ def rc_ring_advance(ring: RcRing, n: int) -> None:
     check(lib().rc_ring_advance(ctypes.byref(ring), n))
 
 
+def rc_key_mass(ring: RcRing, q, n_q: int, q_pos0: int, q_block0: int, q_block_len: int, cache_bias: float,
+                softmax_scale: float, lse, mass, workspace, workspace_bytes: int, stream=None) -> None:
+    check(lib().rc_key_mass(ctypes.byref(ring), _ptr(q), n_q, q_pos0, q_block0, q_block_len, float(cache_bias),
+                            float(softmax_scale), _ptr(lse), _ptr(mass), _ptr(workspace), workspace_bytes,
+                            _stream(stream)))
+
+
+def rc_key_mass_workspace_bytes(ring: RcRing, n_q: int) -> int:
+    return lib().rc_key_mass_workspace_bytes(ctypes.byref(ring), n_q)
+
+
+def rc_cache_write_scored(ring: RcRing, k_new, v_new, n_new: int, pos0: int, block_id: int, key_score,
+                          diversity: float, workspace, workspace_bytes: int, stream=None) -> None:
+    check(lib().rc_cache_write_scored(ctypes.byref(ring), _ptr(k_new), _ptr(v_new), n_new, pos0, block_id,
+                                      _ptr(key_score), float(diversity), _ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
+
+
+def rc_cache_write_scored_workspace_bytes(ring: RcRing, n_new: int) -> int:
+    return lib().rc_cache_write_scored_workspace_bytes(ctypes.byref(ring), n_new)
+
+
 def rc_debug_visibility(ring: RcRing, n_q: int, q_block0: int, q_block_len: int, mask, stream=None) -> None:
     check(lib().rc_debug_visibility(ctypes.byref(ring), n_q, q_block0, q_block_len, _ptr(mask),
                                     _stream(stream)))
@@ -106,7 +131,7 @@ class Ring:
 
     def __init__(self, n_slots: int, n_heads: int, head_dim: int, kv_dtype: str = "fp8",
                  rope_base: float = 10000.0, first_slot: int = 0, n_anchor: int = 0,
-                 device="cuda", stream=None):
+                 n_memory: int = 0, device="cuda", stream=None):
         self.kv = DTYPES[kv_dtype]
         self.kv_name = kv_dtype
         self.device = torch.device(device)
@@ -120,6 +145,7 @@ class Ring:
         s.rope_base = rope_base
         s.v_ld = rc_ring_v_ld(n_slots)
         s.n_anchor = n_anchor
+        s.n_memory = n_memory
         s.k, s.v, s.k_scale, s.v_scale, s.slot_pos, s.slot_block = (_ptr(b) for b in self.buffers)
         rc_ring_init(s, first_slot, stream)
 
@@ -129,11 +155,12 @@ class Ring:
     d = property(lambda self: self.struct.head_dim)
     v_ld = property(lambda self: self.struct.v_ld)
     n_anchor = property(lambda self: self.struct.n_anchor)
+    n_memory = property(lambda self: self.struct.n_memory)
     input_dtype = property(lambda self: _input_dtype(self.kv))
 
-    def state(self) -> tuple[int, int, int, int, int]:
+    def state(self) -> tuple[int, int, int, int, int, int]:
         s = self.struct
-        return (s.head, s.n_hist, s.n_cur, s.cur_pos0, s.cur_block)
+        return (s.head, s.n_hist, s.n_cur, s.cur_pos0, s.cur_block, s.n_mem)
 
     def write(self, k_new, v_new, pos0: int, block_id: int, stream=None) -> None:
         n = k_new.shape[0]
@@ -141,6 +168,38 @@ class Ring:
         _check_tensor(k_new, "k_new", self.input_dtype, shape, self.device)
         _check_tensor(v_new, "v_new", self.input_dtype, shape, self.device)
         rc_cache_write(self.struct, k_new, v_new, n, pos0, block_id, stream)
+
+    def write_scored(self, k_new, v_new, pos0: int, block_id: int, key_score, diversity: float = 1.0,
+                     workspace=None, stream=None) -> None:
+        n = k_new.shape[0]
+        shape = (n, self.H, self.d)
+        _check_tensor(k_new, "k_new", self.input_dtype, shape, self.device)
+        _check_tensor(v_new, "v_new", self.input_dtype, shape, self.device)
+        _check_tensor(key_score, "key_score", torch.float32, (self.H, self.v_ld), self.device)
+        if workspace is None:
+            need = rc_cache_write_scored_workspace_bytes(self.struct, n)
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device) if need else None
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc_cache_write_scored(self.struct, k_new, v_new, n, pos0, block_id, key_score, diversity, workspace,
+                              ws_bytes, stream)
+
+    def key_mass(self, q, q_pos0: int, q_block0: int, q_block_len: int | None, cache_bias: float, lse,
+                 mass=None, softmax_scale: float = 0.0, workspace=None, stream=None):
+        """Accumulate the attention mass of q's rows into mass [H][v_ld]
+        (a new zero tensor when None); lse is rc_chunk_attention's output."""
+        n_q = q.shape[0]
+        _check_tensor(q, "q", self.input_dtype, (n_q, self.H, self.d), self.device)
+        _check_tensor(lse, "lse", torch.float32, (self.H, n_q), self.device)
+        if mass is None:
+            mass = torch.zeros((self.H, self.v_ld), dtype=torch.float32, device=self.device)
+        _check_tensor(mass, "mass", torch.float32, (self.H, self.v_ld), self.device)
+        if workspace is None:
+            need = rc_key_mass_workspace_bytes(self.struct, n_q)
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc_key_mass(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias, softmax_scale, lse,
+                    mass, workspace, ws_bytes, stream)
+        return mass
 
     def rerotate(self, delta: int, stream=None) -> None:
         rc_cache_rerotate(self.struct, delta, stream)

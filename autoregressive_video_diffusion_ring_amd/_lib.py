@@ -22,11 +22,11 @@ class RcRing(ctypes.Structure):
 
     _fields_ = [
         ("n_slots", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("kv_dtype", c_int32),
-        ("rope_base", c_float), ("v_ld", c_int32), ("n_anchor", c_int32),
+        ("rope_base", c_float), ("v_ld", c_int32), ("n_anchor", c_int32), ("n_memory", c_int32),
         ("k", c_void_p), ("v", c_void_p), ("k_scale", c_void_p), ("v_scale", c_void_p),
         ("slot_pos", c_void_p), ("slot_block", c_void_p),
         ("head", c_int32), ("n_hist", c_int32), ("n_cur", c_int32), ("cur_pos0", c_int32),
-        ("cur_block", c_int32),
+        ("cur_block", c_int32), ("n_mem", c_int32),
     ]
 
 
@@ -49,6 +49,12 @@ SIGNATURES = {
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "rc_attention_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
     "rc_ring_advance": (c_int32, [POINTER(RcRing), c_int32]),
+    "rc_key_mass": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,
+                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "rc_key_mass_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
+    "rc_cache_write_scored": (c_int32, [POINTER(RcRing), c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                        c_float, c_void_p, c_size_t, c_void_p]),
+    "rc_cache_write_scored_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
     "rc_debug_visibility": (c_int32, [POINTER(RcRing), c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "rc_last_error": (c_char_p, []),
 }

@@ -8,10 +8,10 @@
 // in flight: every thread issues all of its loads before any arithmetic.
 //
 // Write layout: the written range is cut into at most two linear slot
-// ranges, [head, min(head + n, N)) and the part past slot N-1, which wraps to
-// the first slot of the ring part (slot 0, or the first slot after the pinned
-// anchor slots), and each range into 32-slot chunks aligned to multiples of
-// 32.  One workgroup handles one chunk for kWHeads heads:
+// ranges, [head, min(head + n, E)) and the part past slot E-1 (E = N, or the
+// first content-memory slot), which wraps to the first slot of the ring part
+// (slot 0, or the first slot after the pinned anchor slots), and each range
+// into 32-slot chunks aligned to multiples of 32.  One workgroup handles one chunk for kWHeads heads:
 //  * a row (one token of one head, d elements) is handled by 16 lanes with
 //    d/16 contiguous elements each, so a row's loads and stores are whole
 //    contiguous cache rows; a thread takes 4 consecutive slots of one head;
@@ -62,6 +62,7 @@ struct WriteArgs {
   const void* v_new;
   int n_new, head, pos0, block_id;
   int lo_a, hi_a, lo_b, hi_b, chunks_a;
+  int wrap_tok;       // token index of slot lo_b minus lo_b + head (the wrapped range's offset)
   int chunks, items;  // chunks per head group; chunks x head groups
   int grid;           // workgroups launched (a multiple of 8)
   int use_rope;
@@ -205,12 +206,13 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   // Every argument used before the first input load is read here in one
   // batch of scalar loads; the empty asm keeps them from being spread over
   // the dependent steps below (one argument round trip instead of several).
-  const int N = a.r.N, H = a.r.H, grid = a.grid, items = a.items, chunks = a.chunks;
+  const int H = a.r.H, grid = a.grid, items = a.items, chunks = a.chunks;
   const int chunks_a = a.chunks_a, lo_a = a.lo_a, hi_a = a.hi_a, lo_b = a.lo_b, hi_b = a.hi_b, head = a.head;
+  const int wrap_tok = a.wrap_tok;
   const void* const k_new = a.k_new;
   const void* const v_new = a.v_new;
-  asm volatile("" ::"s"(N), "s"(H), "s"(grid), "s"(items), "s"(chunks), "s"(chunks_a), "s"(lo_a), "s"(hi_a),
-               "s"(lo_b), "s"(hi_b), "s"(head), "s"(k_new), "s"(v_new));
+  asm volatile("" ::"s"(H), "s"(grid), "s"(items), "s"(chunks), "s"(chunks_a), "s"(lo_a), "s"(hi_a),
+               "s"(lo_b), "s"(hi_b), "s"(head), "s"(wrap_tok), "s"(k_new), "s"(v_new));
   // Workgroups are dealt to the 8 XCDs in turn; give each XCD a contiguous
   // range of work items, so that the neighbouring chunks whose V^T pieces
   // share 128-byte lines are written through the same L2.
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   }
   // token index of slot s (slots of one chunk have consecutive tokens): slots
   // from head on hold tokens 0.., the wrapped range [lo_b, hi_b) (below head)
-  // continues with token N - head
+  // continues with token E - head, E the end of the ring part
   auto token_of = [&](int s) {
     int t = s - head;
-    return t < 0 ? t + (N - lo_b) : t;
+    return t < 0 ? t + wrap_tok : t;
   };
   const int piece = tid % kLanesPerRow;
   const int rg = tid / kLanesPerRow;
@@ -507,11 +509,14 @@ hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* 
   a.head = head;
   a.pos0 = pos0;
   a.block_id = block_id;
+  // the ring part is slots n_anchor .. E-1; the part of the write past
+  // slot E-1 wraps to its first slot
+  const int E = r.N - r.n_memory;
   a.lo_a = head;
-  a.hi_a = std::min(head + n_new, r.N);
-  // the part past slot N-1 wraps to the first slot of the ring part
+  a.hi_a = std::min(head + n_new, E);
   a.lo_b = r.n_anchor;
-  a.hi_b = head + n_new > r.N ? r.n_anchor + head + n_new - r.N : r.n_anchor;
+  a.hi_b = head + n_new > E ? r.n_anchor + head + n_new - E : r.n_anchor;
+  a.wrap_tok = E - r.n_anchor;
   a.chunks_a = (a.hi_a - 1) / kWChunk - a.lo_a / kWChunk + 1;
   const int chunks_b = a.hi_b > a.lo_b ? (a.hi_b - 1) / kWChunk - a.lo_b / kWChunk + 1 : 0;
   a.use_rope = r.rope_base > 0.f;

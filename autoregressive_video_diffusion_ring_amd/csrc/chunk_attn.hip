@@ -285,18 +285,6 @@ __device__ __forceinline__ int q_dim(int g, int e) {
   else return 2 * e + g;
 }
 
-// cos and sin of pos * theta_j for the queries: the angle is reduced in
-// float64 to at most half a revolution, then the hardware sine and cosine
-// (which take revolutions) finish it.  Q is rounded to FP8 or BF16 (or kept
-// in float32 for the F32 cache, whose tolerance is far above this error).
-__device__ __forceinline__ void rope_cs_hw(double rev, long long pos, float* c, float* s) {
-  double r = static_cast<double>(pos) * rev;
-  r -= rint(r);
-  const float t = static_cast<float>(r);
-  *s = __builtin_amdgcn_sinf(t);
-  *c = __builtin_amdgcn_cosf(t);
-}
-
 // Four floats to four e4m3 codes written over `old`; both halves of the word
 // are replaced, so passing the word's previous value avoids clearing it.
 __device__ __forceinline__ int cvt_fp8x4_over(float a, float b, float c, float d, int old) {

@@ -69,6 +69,19 @@ __device__ __forceinline__ void rope_cs_rev(double rev, long long pos, float* c,
   sincosf(static_cast<float>(r * 6.283185307179586476925286766559), s, c);
 }
 
+// cos and sin of pos * theta_j for queries: the angle is reduced in float64
+// to at most half a revolution, then the hardware sine and cosine (which take
+// revolutions; error about 2^-23 on that range) finish it.  Queries are
+// rounded to FP8 or BF16 afterwards (or kept in float32 for the F32 cache,
+// whose tolerance is far above this error).
+__device__ __forceinline__ void rope_cs_hw(double rev, long long pos, float* c, float* s) {
+  double r = static_cast<double>(pos) * rev;
+  r -= rint(r);
+  const float t = static_cast<float>(r);
+  *s = __builtin_amdgcn_sinf(t);
+  *c = __builtin_amdgcn_cosf(t);
+}
+
 // ---------------------------------------------------------------- masks
 // Block-causal visibility of a cached slot (block id kb, -1 = never written)
 // to a query of block qb: invisible, visible, or visible with the cache bias

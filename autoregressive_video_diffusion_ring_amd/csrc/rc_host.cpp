@@ -8,11 +8,13 @@
 // min(n_hist, N - n).  The chunk stays "current" (n_cur = n) through its
 // denoising passes, each of which writes the same slots again, until
 // rc_ring_advance commits it: head += n (mod N), n_hist += n, n_cur = 0.
-// With an anchor of A slots the ring part is slots A..N-1: every wrap goes
-// from N back to A, so the first A tokens of the stream stay in slots 0..A-1
-// (the anchor starts filling at slot 0), and a chunk holds at most N - A
-// tokens.  n_hist keeps the same update rules: a write evicts the oldest
-// tokens of the ring part only.
+// With an anchor of A slots and a content memory of M slots the ring part
+// is slots A..E-1, E = N - M: every wrap goes from E back to A, so the first
+// A tokens of the stream stay in slots 0..A-1 (the anchor starts filling at
+// slot 0), and a chunk holds at most E - A tokens.  n_hist counts anchor and
+// ring-part tokens (at most E); a write evicts the oldest tokens of the ring
+// part only.  The memory slots E..N-1 are filled only by scored writes, which
+// keep them a prefix: n_mem occupied slots are E..E+n_mem-1.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -29,8 +31,9 @@
 #include "rc_kernels.h"
 
 // The layout the Python binding mirrors.
-static_assert(offsetof(rc_ring, n_anchor) == 24 && offsetof(rc_ring, k) == 32, "rc_ring layout");
-static_assert(offsetof(rc_ring, head) == 80 && sizeof(rc_ring) == 104, "rc_ring layout");
+static_assert(offsetof(rc_ring, n_anchor) == 24 && offsetof(rc_ring, n_memory) == 28, "rc_ring layout");
+static_assert(offsetof(rc_ring, k) == 32 && offsetof(rc_ring, head) == 80, "rc_ring layout");
+static_assert(offsetof(rc_ring, n_mem) == 100 && sizeof(rc_ring) == 104, "rc_ring layout");
 
 namespace {
 
@@ -76,8 +79,9 @@ rc_status check_ring(const rc_ring* r) {
   if (r->v_ld != rc_ring_v_ld(r->n_slots))
     return fail(RC_ERR_ARG, "v_ld must be rc_ring_v_ld(n_slots) = %d (got %d)", rc_ring_v_ld(r->n_slots), r->v_ld);
   if (!std::isfinite(r->rope_base) || r->rope_base < 0.f) return fail(RC_ERR_ARG, "rope_base must be >= 0");
-  if (r->n_anchor < 0 || r->n_anchor >= r->n_slots)
-    return fail(RC_ERR_ARG, "n_anchor must be in 0..%d (got %d)", r->n_slots - 1, r->n_anchor);
+  if (r->n_anchor < 0 || r->n_memory < 0 || static_cast<long long>(r->n_anchor) + r->n_memory >= r->n_slots)
+    return fail(RC_ERR_ARG, "need n_anchor >= 0, n_memory >= 0, n_anchor + n_memory < N (got %d, %d, N %d)",
+                r->n_anchor, r->n_memory, r->n_slots);
   if (!r->k || !r->v || !r->slot_pos || !r->slot_block) return fail(RC_ERR_ARG, "ring device pointer is NULL");
   if (r->kv_dtype == RC_FP8_E4M3 && (!r->k_scale || !r->v_scale))
     return fail(RC_ERR_ARG, "FP8 ring needs k_scale and v_scale");
@@ -86,11 +90,15 @@ rc_status check_ring(const rc_ring* r) {
   return RC_OK;
 }
 
+// End of the ring part (first memory slot).
+int32_t ring_end(const rc_ring* r) { return r->n_slots - r->n_memory; }
+
 rc_status check_state(const rc_ring* r) {
-  const int N = r->n_slots;
-  if (r->head < 0 || r->head >= N || r->n_hist < 0 || r->n_cur < 0 || r->n_hist + r->n_cur > N)
-    return fail(RC_ERR_STATE, "ring host state is corrupt (head %d, n_hist %d, n_cur %d, N %d)", r->head,
-                r->n_hist, r->n_cur, N);
+  const int E = ring_end(r);
+  if (r->head < 0 || r->head >= E || r->n_hist < 0 || r->n_cur < 0 || r->n_hist + r->n_cur > E ||
+      r->n_mem < 0 || r->n_mem > r->n_memory)
+    return fail(RC_ERR_STATE, "ring host state is corrupt (head %d, n_hist %d, n_cur %d, n_mem %d, E %d)", r->head,
+                r->n_hist, r->n_cur, r->n_mem, E);
   return RC_OK;
 }
 
@@ -102,6 +110,7 @@ rc::RingView view(const rc_ring* r) {
   v.kv = r->kv_dtype;
   v.v_ld = r->v_ld;
   v.n_anchor = r->n_anchor;
+  v.n_memory = r->n_memory;
   v.rope_base = r->rope_base;
   v.k = r->k;
   v.v = r->v;
@@ -114,11 +123,45 @@ rc::RingView view(const rc_ring* r) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// The slot n places after `head`, wrapping from N to the ring part's first
-// slot (n_anchor); n <= N - n_anchor.
+// The slot n places after `head`, wrapping from the ring part's end E to its
+// first slot (n_anchor); n <= E - n_anchor.
 int32_t step_slot(const rc_ring* r, int32_t head, int32_t n) {
   const int32_t s = head + n;
-  return s < r->n_slots ? s : s - r->n_slots + r->n_anchor;
+  const int32_t E = ring_end(r);
+  return s < E ? s : s - E + r->n_anchor;
+}
+
+// Argument and state checks shared by both writes.
+rc_status check_write(const rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0,
+                      int32_t block_id) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if ((st = check_state(r)) != RC_OK) return st;
+  if (!k_new || !v_new) return fail(RC_ERR_ARG, "k_new / v_new is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
+    return fail(RC_ERR_ARG, "k_new and v_new must be 16-byte aligned");
+  const int32_t cap = ring_end(r) - r->n_anchor;
+  if (n_new < 1 || n_new > cap)
+    return fail(RC_ERR_ARG, "n_new must be in 1..%d (N - n_anchor - n_memory; got %d)", cap, n_new);
+  if (block_id < 0) return fail(RC_ERR_ARG, "block_id must be >= 0 (got %d)", block_id);
+  if (static_cast<long long>(pos0) + n_new - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (r->n_cur > 0 && (n_new != r->n_cur || pos0 != r->cur_pos0 || block_id != r->cur_block))
+    return fail(RC_ERR_STATE,
+                "chunk (n %d, pos0 %d, block %d) is current; a rewrite must repeat it (got n %d, pos0 %d, block %d)",
+                r->n_cur, r->cur_pos0, r->cur_block, n_new, pos0, block_id);
+  return RC_OK;
+}
+
+// Launch the write and update the host state.
+rc_status do_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0, int32_t block_id,
+                   hipStream_t stream) {
+  hipError_t e = rc::launch_cache_write(view(r), k_new, v_new, n_new, r->head, pos0, block_id, stream);
+  if (e != hipSuccess) return hip_fail(e, "cache write");
+  if (r->n_cur == 0) r->n_hist = std::min(r->n_hist, ring_end(r) - n_new);
+  r->n_cur = n_new;
+  r->cur_pos0 = pos0;
+  r->cur_block = block_id;
+  return ok();
 }
 
 }  // namespace
@@ -150,6 +193,8 @@ rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
     return fail(RC_ERR_ARG, "first_slot must be in 0..%d (got %d)", r->n_slots - 1, first_slot);
   if (r->n_anchor > 0 && first_slot != 0)
     return fail(RC_ERR_ARG, "a ring with an anchor starts at slot 0 (got first_slot %d)", first_slot);
+  if (first_slot >= ring_end(r))
+    return fail(RC_ERR_ARG, "first_slot must lie before the memory slots (got %d, E %d)", first_slot, ring_end(r));
   hipError_t e = rc::launch_ring_clear(view(r), as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "ring clear");
   r->head = first_slot;
@@ -157,32 +202,51 @@ rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
   r->n_cur = 0;
   r->cur_pos0 = 0;
   r->cur_block = 0;
+  r->n_mem = 0;
   return ok();
 }
 
 rc_status rc_cache_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0,
                          int32_t block_id, void* stream) {
-  rc_status st = check_ring(r);
+  rc_status st = check_write(r, k_new, v_new, n_new, pos0, block_id);
   if (st != RC_OK) return st;
-  if ((st = check_state(r)) != RC_OK) return st;
-  if (!k_new || !v_new) return fail(RC_ERR_ARG, "k_new / v_new is NULL");
-  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
-    return fail(RC_ERR_ARG, "k_new and v_new must be 16-byte aligned");
-  if (n_new < 1 || n_new > r->n_slots - r->n_anchor)
-    return fail(RC_ERR_ARG, "n_new must be in 1..%d (N - n_anchor; got %d)", r->n_slots - r->n_anchor, n_new);
-  if (block_id < 0) return fail(RC_ERR_ARG, "block_id must be >= 0 (got %d)", block_id);
-  if (static_cast<long long>(pos0) + n_new - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
-  if (r->n_cur > 0 && (n_new != r->n_cur || pos0 != r->cur_pos0 || block_id != r->cur_block))
-    return fail(RC_ERR_STATE,
-                "chunk (n %d, pos0 %d, block %d) is current; a rewrite must repeat it (got n %d, pos0 %d, block %d)",
-                r->n_cur, r->cur_pos0, r->cur_block, n_new, pos0, block_id);
-  hipError_t e = rc::launch_cache_write(view(r), k_new, v_new, n_new, r->head, pos0, block_id, as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e, "cache write");
-  if (r->n_cur == 0) r->n_hist = std::min(r->n_hist, r->n_slots - n_new);
-  r->n_cur = n_new;
-  r->cur_pos0 = pos0;
-  r->cur_block = block_id;
-  return ok();
+  return do_write(r, k_new, v_new, n_new, pos0, block_id, as_stream(stream));
+}
+
+size_t rc_cache_write_scored_workspace_bytes(const rc_ring* r, int32_t n_new) {
+  if (check_ring(r) != RC_OK || n_new < 1) return 0;
+  return rc::memory_workspace_bytes(r->n_memory, n_new);
+}
+
+rc_status rc_cache_write_scored(rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0,
+                                int32_t block_id, const float* key_score, float diversity, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  rc_status st = check_write(r, k_new, v_new, n_new, pos0, block_id);
+  if (st != RC_OK) return st;
+  const int32_t E = ring_end(r);
+  // history tokens this write overwrites (none on a rewrite of the current chunk)
+  const int32_t evicted = r->n_cur == 0 ? r->n_hist - std::min(r->n_hist, E - n_new) : 0;
+  const bool update = r->n_memory > 0 && evicted > 0;
+  if (r->n_memory > 0 && r->n_cur == 0) {
+    if (!(diversity > 0.f && diversity <= 1.f)) return fail(RC_ERR_ARG, "diversity must be in (0, 1]");
+    if (!key_score) return fail(RC_ERR_ARG, "key_score is NULL");
+    if (reinterpret_cast<uintptr_t>(key_score) & 3u) return fail(RC_ERR_ARG, "key_score must be 4-byte aligned");
+    if (static_cast<long long>(r->n_memory) + n_new > rc::kMaxMemoryCandidates)
+      return fail(RC_ERR_UNSUPPORTED, "n_memory + n_new must be <= %d (got %d + %d)", rc::kMaxMemoryCandidates,
+                  r->n_memory, n_new);
+    const size_t need = rc::memory_workspace_bytes(r->n_memory, n_new);
+    if (!workspace || workspace_bytes < need)
+      return fail(RC_ERR_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(RC_ERR_ARG, "workspace must be 16-byte aligned");
+  }
+  if (update) {
+    hipError_t e = rc::launch_memory_update(view(r), key_score, diversity, r->head, n_new, workspace,
+                                            as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "memory update");
+  }
+  st = do_write(r, k_new, v_new, n_new, pos0, block_id, as_stream(stream));
+  if (st == RC_OK && update) r->n_mem = std::min(r->n_memory, r->n_mem + evicted);
+  return st;
 }
 
 rc_status rc_cache_rerotate(rc_ring* r, int32_t delta, void* stream) {
@@ -229,16 +293,52 @@ rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32
   return ok();
 }
 
+size_t rc_key_mass_workspace_bytes(const rc_ring* r, int32_t n_q) {
+  if (check_ring(r) != RC_OK || n_q < 1) return 0;
+  return rc::key_mass_workspace_bytes(view(r), n_q);
+}
+
+rc_status rc_key_mass(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                      int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse, float* mass,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if (!rc::key_mass_supported(r->kv_dtype, r->head_dim))
+    return fail(RC_ERR_UNSUPPORTED, "key mass is built for FP8 rings only");
+  if (!q || !lse || !mass) return fail(RC_ERR_ARG, "q / lse / mass is NULL");
+  if (reinterpret_cast<uintptr_t>(q) & 15u) return fail(RC_ERR_ARG, "q must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(mass)) & 3u)
+    return fail(RC_ERR_ARG, "lse and mass must be 4-byte aligned");
+  if (n_q < 1) return fail(RC_ERR_ARG, "n_q must be >= 1 (got %d)", n_q);
+  if (q_block_len < 1) return fail(RC_ERR_ARG, "q_block_len must be >= 1 (got %d)", q_block_len);
+  if (static_cast<long long>(q_pos0) + n_q - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (!std::isfinite(cache_bias) && !(cache_bias < 0.f))
+    return fail(RC_ERR_ARG, "cache_bias must be finite or -inf");
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(RC_ERR_ARG, "softmax_scale must be finite and >= 0");
+  const size_t need = rc::key_mass_workspace_bytes(view(r), n_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(RC_ERR_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(RC_ERR_ARG, "workspace must be 16-byte aligned");
+  rc::AttnCall c{q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, nullptr, nullptr, workspace,
+                 workspace_bytes};
+  hipError_t e = rc::launch_key_mass(view(r), c, lse, mass, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "key mass");
+  return ok();
+}
+
 rc_status rc_ring_advance(rc_ring* r, int32_t n) {
   if (!r) return fail(RC_ERR_ARG, "ring is NULL");
-  if (r->n_slots < 1 || r->n_anchor < 0 || r->n_anchor >= r->n_slots)
-    return fail(RC_ERR_ARG, "bad n_slots / n_anchor (%d / %d)", r->n_slots, r->n_anchor);
+  if (r->n_slots < 1 || r->n_anchor < 0 || r->n_memory < 0 ||
+      static_cast<long long>(r->n_anchor) + r->n_memory >= r->n_slots)
+    return fail(RC_ERR_ARG, "bad n_slots / n_anchor / n_memory (%d / %d / %d)", r->n_slots, r->n_anchor,
+                r->n_memory);
   rc_status st = check_state(r);
   if (st != RC_OK) return st;
   if (r->n_cur == 0 || n != r->n_cur)
     return fail(RC_ERR_STATE, "advance(%d) needs n == n_cur > 0 (n_cur %d)", n, r->n_cur);
   r->head = step_slot(r, r->head, n);
-  r->n_hist = std::min(r->n_hist + n, r->n_slots);
+  r->n_hist = std::min(r->n_hist + n, ring_end(r));
   r->n_cur = 0;
   return ok();
 }

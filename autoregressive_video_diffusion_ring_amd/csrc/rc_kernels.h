@@ -11,7 +11,9 @@ namespace rc {
 struct RingView {
   int N, H, d, kv, v_ld;
   float rope_base;
-  int n_anchor;  // slots 0..n_anchor-1 are pinned; writes wrap from N to n_anchor
+  int n_anchor;  // slots 0..n_anchor-1 are pinned
+  int n_memory;  // slots N-n_memory..N-1 are the content memory; writes wrap from
+                 // E = N - n_memory to n_anchor
   void* k;
   void* v;
   float* k_scale;
@@ -24,8 +26,8 @@ enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 hipError_t launch_ring_clear(const RingView& r, hipStream_t s);
 
-// Writes n_new tokens to slots head + i, wrapping from N to n_anchor
-// (n_new <= N - n_anchor).
+// Writes n_new tokens to slots head + i, wrapping from E to n_anchor
+// (n_new <= E - n_anchor).
 hipError_t launch_cache_write(const RingView& r, const void* k_new, const void* v_new, int n_new,
                               int head, int pos0, int block_id, hipStream_t s);
 
@@ -47,6 +49,20 @@ bool attention_supported(int kv, int d);
 int attention_splits(const RingView& r, int n_q);
 size_t attention_workspace_bytes(const RingView& r, int n_q);
 hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStream_t s);
+
+// Attention mass per head and slot (memory.hip).
+bool key_mass_supported(int kv, int d);
+size_t key_mass_workspace_bytes(const RingView& r, int n_q);
+hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* lse, float* mass,
+                           hipStream_t s);
+
+// Scored content memory (memory.hip): before a write of n_new tokens at
+// `head`, keep the best of the memory's tokens and the history tokens the
+// write evicts in the memory slots.
+constexpr int kMaxMemoryCandidates = 4096;
+size_t memory_workspace_bytes(int n_memory, int n_new);
+hipError_t launch_memory_update(const RingView& r, const float* key_score, float gamma, int head, int n_new,
+                                void* workspace, hipStream_t s);
 
 hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
                                    uint8_t* mask, hipStream_t s);

@@ -74,11 +74,20 @@ typedef enum {
  * from slot N-1 to slot A instead of slot 0.  An anchored ring starts at slot 0
  * and its chunks hold at most N - A tokens.  Attention and re-rotation treat
  * anchor slots like any other written slot.
+ * Content memory (StreamLTX project page, "Why a long take does not slow
+ * down": an anchor, a content memory and a FIFO of recent blocks, each layer
+ * scoring its own keys and keeping a top-M budget).  With n_memory = M > 0 the
+ * last M slots, E = N - M .. N-1, are the memory and the sliding part is
+ * A..E-1: writes wrap from E to A and a chunk holds at most E - A tokens.
+ * rc_cache_write lets the history tokens it overwrites go; rc_cache_write_scored
+ * first keeps the best of them in the memory.  Memory slots are read by
+ * attention and moved by re-rotation like any other written slot.
  * Host state (maintained by the library; read it, do not write it):
  *   head       next slot to write
- *   n_hist     committed history tokens in the cache
+ *   n_hist     committed history tokens in the anchor and sliding part (<= E)
  *   n_cur      tokens of the current, not yet committed, chunk (0 = none)
  *   cur_pos0, cur_block   position of the current chunk's first token, its block
+ *   n_mem      occupied memory slots; they are always slots E .. E + n_mem - 1
  */
 typedef struct rc_ring {
   int32_t n_slots;     /* N >= 1 */
@@ -87,14 +96,15 @@ typedef struct rc_ring {
   int32_t kv_dtype;    /* rc_dtype */
   float rope_base;     /* RoPE base (10000 on the pages' workloads); 0 = no RoPE */
   int32_t v_ld;        /* must equal rc_ring_v_ld(n_slots) */
-  int32_t n_anchor;    /* A pinned slots, 0 <= A < N (0 = plain ring); see below */
+  int32_t n_anchor;    /* A pinned slots at the start (0 = none); see below */
+  int32_t n_memory;    /* M content-memory slots at the end (0 = none); A + M < N */
   void* k;
   void* v;
   float* k_scale;
   float* v_scale;
   int32_t* slot_pos;
   int32_t* slot_block;
-  int32_t head, n_hist, n_cur, cur_pos0, cur_block;
+  int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem;
 } rc_ring;
 
 /* Leading dimension of the transposed V buffer: N rounded up to 64. */
@@ -111,15 +121,15 @@ rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int3
 /*
  * Validate the geometry and pointers, zero K, V and the scales, set every
  * slot_block to -1 and slot_pos to 0 (asynchronously on `stream`), and set the
- * host state: head = first_slot (0 <= first_slot < N; 0 when n_anchor > 0),
- * n_hist = n_cur = 0.
+ * host state: head = first_slot (0 <= first_slot < N - n_memory; 0 when
+ * n_anchor > 0), n_hist = n_cur = n_mem = 0.
  */
 rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
 
 /*
- * Write n_new tokens into slots head + i, i < n_new, wrapping from N to
- * n_anchor (so (head + i) mod N without an anchor) (Runway Characters,
- * abstract: ring cache, RoPE and FP8 quantisation once per write).
+ * Write n_new tokens into slots head + i, i < n_new, wrapping from E = N -
+ * n_memory to n_anchor (so (head + i) mod N for the plain ring) (Runway
+ * Characters, abstract: ring cache, RoPE and FP8 quantisation once per write).
  *   k_new, v_new  device [n_new][H][d], bfloat16 (float32 for an RC_F32 ring),
  *                 token-major as a QKV projection produces them
  *   pos0          position of token 0; token i has position pos0 + i
@@ -129,9 +139,9 @@ rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
  * codes = round-to-nearest-even(x / scale); for BF16 rings the values are
  * rounded to bfloat16.  slot_pos and slot_block are set for the written slots.
  * History slots overwritten by the write are evicted: n_hist becomes
- * min(n_hist, N - n_new).  Every denoising pass of one chunk writes again
+ * min(n_hist, E - n_new).  Every denoising pass of one chunk writes again
  * before rc_ring_advance: while n_cur > 0, n_new, pos0 and block_id must repeat
- * the current chunk's, else RC_ERR_STATE.  Requires 1 <= n_new <= N - n_anchor.
+ * the current chunk's, else RC_ERR_STATE.  Requires 1 <= n_new <= E - n_anchor.
  */
 rc_status rc_cache_write(rc_ring* ring, const void* k_new, const void* v_new, int32_t n_new,
                          int32_t pos0, int32_t block_id, void* stream);
@@ -177,10 +187,70 @@ size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
 
 /*
  * Commit the current chunk as history (host only, nothing is enqueued):
- * head moves n slots on (wrapping from N to n_anchor), n_hist =
- * min(n_hist + n, N), n_cur = 0.  Requires n == n_cur > 0.
+ * head moves n slots on (wrapping from E to n_anchor), n_hist =
+ * min(n_hist + n, E), n_cur = 0.  Requires n == n_cur > 0.
  */
 rc_status rc_ring_advance(rc_ring* ring, int32_t n);
+
+/*
+ * Attention mass per head and slot, the attention quality by which a layer
+ * scores its keys (StreamLTX project page, "Why a long take does not slow
+ * down"): mass[h][s] += sum over queries i of p_h(i, s), where p is the
+ * block-causal softmax of rc_chunk_attention with the same arguments,
+ * normalised by the lse that call returned.
+ *   q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale
+ *              as for rc_chunk_attention
+ *   lse        device [H][n_q] float32: that call's lse output
+ *   mass       device [H][v_ld] float32, accumulated into (the caller clears
+ *              it); invisible slots and padding entries get += 0
+ *   workspace  device scratch of rc_key_mass_workspace_bytes(ring, n_q) bytes
+ * Products are taken in FP8 (queries quantised per 32 queries) like the
+ * attention; every mass entry is summed by one wave in a fixed order (no
+ * atomics), so results are reproducible.  FP8 rings only (RC_ERR_UNSUPPORTED
+ * otherwise).
+ */
+rc_status rc_key_mass(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                      int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse, float* mass,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace rc_key_mass needs for n_q queries (0 for a bad ring or n_q). */
+size_t rc_key_mass_workspace_bytes(const rc_ring* ring, int32_t n_q);
+
+/*
+ * rc_cache_write with a scored content memory.  On the first pass of a chunk
+ * (n_cur == 0) of a ring with n_memory = M > 0, the history tokens the write
+ * will overwrite compete with the tokens in the memory for its M slots before
+ * they are overwritten (StreamLTX project page, "Why a long take does not
+ * slow down": each layer scores its keys on attention quality and temporal
+ * diversity and keeps a top-M budget):
+ *   key_score  device [H][v_ld] float32, finite and >= 0 (rc_key_mass of the
+ *              previous chunk's queries, say).  A slot's score Q is the
+ *              float64 sum of its H entries in head order.
+ *   diversity  gamma in (0, 1].  The memory keeps the min(M, candidates)
+ *              tokens that maximise the sum over blocks of
+ *              sum_k Q_(k) gamma^k, Q_(0) >= Q_(1) >= ... the kept scores of
+ *              one block: gamma = 1 is top-M by score, a smaller gamma
+ *              spreads the memory over more blocks.  The choice is the greedy
+ *              one: each block offers its best remaining token (higher Q,
+ *              then lower slot) with gain Q gamma^c (c tokens of the block
+ *              already kept; gamma^c the float64 product of c factors of the
+ *              float32 gamma); the largest gain is kept, ties to the smaller
+ *              c, then the lower slot.
+ *   workspace  device scratch of rc_cache_write_scored_workspace_bytes(ring,
+ *              n_new) bytes
+ * Kept tokens from the sliding part move (K, V, scales, position, block) into
+ * the memory slots that hold no kept token, both taken in ascending slot
+ * order; then the write proceeds as rc_cache_write.  n_mem becomes
+ * min(M, n_mem + evicted history tokens).  Requires M + n_new <= 4096
+ * (RC_ERR_UNSUPPORTED otherwise).  Without a memory, or on a later pass, this
+ * is rc_cache_write (key_score and workspace are not read).
+ */
+rc_status rc_cache_write_scored(rc_ring* ring, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0,
+                                int32_t block_id, const float* key_score, float diversity, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Workspace rc_cache_write_scored needs for a write of n_new tokens. */
+size_t rc_cache_write_scored_workspace_bytes(const rc_ring* ring, int32_t n_new);
 
 /*
  * The visibility predicate used inside rc_chunk_attention, exported for

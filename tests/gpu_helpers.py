@@ -50,7 +50,8 @@ def oracle_from_gpu(ring: Ring, rope_base: float) -> OracleRing:
     c = gpu_cache(ring)
     return OracleRing.from_arrays(kv_dtype=ring.kv_name, rope_base=rope_base, k=c["k"], v=c["v"],
                                   k_scale=c["k_scale"], v_scale=c["v_scale"], slot_pos=c["slot_pos"],
-                                  slot_block=c["slot_block"], state=c["state"], n_anchor=ring.n_anchor)
+                                  slot_block=c["slot_block"], state=c["state"], n_anchor=ring.n_anchor,
+                                  n_memory=ring.n_memory)
 
 
 def compare_cache(gpu: dict, orc: OracleRing, kv: str, slots=None):

@@ -38,20 +38,21 @@ def test_library_exports_every_header_symbol():
 
 
 def test_struct_layout_matches_c():
-    # int32 x 4, float, int32 x 2, then six pointers at 8-byte alignment, then 5 int32
-    assert RcRing.n_anchor.offset == 24
+    # int32 x 4, float, int32 x 3, then six pointers at 8-byte alignment, then 6 int32
+    # (the library checks the same offsets with static_asserts)
+    assert RcRing.n_anchor.offset == 24 and RcRing.n_memory.offset == 28
     assert RcRing.k.offset == 32 and RcRing.slot_block.offset == 72
-    assert RcRing.head.offset == 80 and RcRing.cur_block.offset == 96
+    assert RcRing.head.offset == 80 and RcRing.cur_block.offset == 96 and RcRing.n_mem.offset == 100
     assert ctypes.sizeof(RcRing) == 104
 
 
 FAKE = 1 << 20  # aligned placeholder address; never dereferenced by the checks below
 
 
-def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0, n_anchor=0):
+def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0, n_anchor=0, n_memory=0):
     r = RcRing()
     r.n_slots, r.n_heads, r.head_dim, r.kv_dtype = N, H, d, kv
-    r.n_anchor = n_anchor
+    r.n_anchor, r.n_memory = n_anchor, n_memory
     r.rope_base = 10000.0
     r.v_ld = lib().rc_ring_v_ld(N)
     r.k = r.v = r.k_scale = r.v_scale = r.slot_pos = r.slot_block = FAKE
@@ -60,7 +61,7 @@ def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0, n_anchor=
 
 
 def state(r):
-    return (r.head, r.n_hist, r.n_cur, r.cur_pos0, r.cur_block)
+    return (r.head, r.n_hist, r.n_cur, r.cur_pos0, r.cur_block, r.n_mem)
 
 
 def test_v_ld_and_sizes():
@@ -76,10 +77,11 @@ def test_v_ld_and_sizes():
     assert L.rc_ring_sizes(10, 2, 64, 7, out) == RC_ERR_ARG
 
 
-@pytest.mark.parametrize("N,n,h0,chunks,A", [(5788, 757, 5031, 30, 0), (96, 32, 0, 9, 0), (10, 10, 3, 4, 0),
-                                             (7, 3, 6, 12, 0), (5788, 757, 0, 30, 757), (10, 3, 0, 12, 3),
-                                             (10, 3, 0, 12, 4), (7, 1, 0, 20, 6)])
-def test_advance_matches_oracle(N, n, h0, chunks, A):
+@pytest.mark.parametrize("N,n,h0,chunks,A,M", [(5788, 757, 5031, 30, 0, 0), (96, 32, 0, 9, 0, 0), (10, 10, 3, 4, 0, 0),
+                                               (7, 3, 6, 12, 0, 0), (5788, 757, 0, 30, 757, 0), (10, 3, 0, 12, 3, 0),
+                                               (10, 3, 0, 12, 4, 0), (7, 1, 0, 20, 6, 0), (5788, 757, 0, 30, 757, 1000),
+                                               (12, 3, 0, 15, 2, 3), (12, 4, 5, 15, 0, 3)])
+def test_advance_matches_oracle(N, n, h0, chunks, A, M):
     """Host bookkeeping of write + advance, bit-exact against the oracle,
     with and without pinned anchor slots.
 
@@ -87,12 +89,12 @@ def test_advance_matches_oracle(N, n, h0, chunks, A):
     replayed by hand exactly as rc_cache_write applies it after a successful
     launch; rc_ring_advance itself runs in the library."""
     L = lib()
-    r = fake_ring(N, head=h0, n_anchor=A)
-    o = OracleRing(N, 1, 2, "f32", 0.0, first_slot=h0, n_anchor=A)
+    r = fake_ring(N, head=h0, n_anchor=A, n_memory=M)
+    o = OracleRing(N, 1, 2, "f32", 0.0, first_slot=h0, n_anchor=A, n_memory=M)
     z = np.zeros((n, 1, 2))
     for t in range(chunks):
         o.write(z, z, n, n * t, t)
-        r.n_hist = min(r.n_hist, N - n)
+        r.n_hist = min(r.n_hist, N - M - n)
         r.n_cur, r.cur_pos0, r.cur_block = n, n * t, t
         assert state(r) == o.state()
         assert L.rc_ring_advance(ctypes.byref(r), n) == RC_OK
@@ -140,7 +142,7 @@ def test_write_argument_and_state_checks():
     assert L.rc_cache_write(ctypes.byref(ra), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
     ra.n_anchor = -1
     assert L.rc_cache_write(ctypes.byref(ra), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
-    assert state(ra) == (0, 0, 0, 0, 0)
+    assert state(ra) == (0, 0, 0, 0, 0, 0)
     r2 = fake_ring(100)
     r2.v_ld = 100  # wrong leading dimension
     assert L.rc_cache_write(ctypes.byref(r2), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
@@ -203,3 +205,63 @@ def test_advance_checks_anchor():
     r.head = 9
     assert L.rc_ring_advance(ctypes.byref(r), 3) == RC_OK
     assert state(r)[:3] == (5, 3, 0)    # 9 -> 3 + (9 + 3 - 10)
+
+
+def test_memory_geometry_checks():
+    L = lib()
+    r = fake_ring(100, n_anchor=40, n_memory=60)   # A + M == N
+    assert L.rc_cache_write(ctypes.byref(r), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
+    r = fake_ring(100, n_memory=-1)
+    assert L.rc_cache_write(ctypes.byref(r), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_ARG
+    r = fake_ring(100, n_memory=30)
+    assert L.rc_ring_init(ctypes.byref(r), 70, None) == RC_ERR_ARG      # first slot inside the memory
+    assert L.rc_cache_write(ctypes.byref(r), FAKE, FAKE, 71, 0, 0, None) == RC_ERR_ARG   # > E - A = 70
+    r.head = 75                                                          # head inside the memory
+    assert L.rc_cache_write(ctypes.byref(r), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_STATE
+    r.head, r.n_mem = 0, 31                                              # n_mem > M
+    assert L.rc_cache_write(ctypes.byref(r), FAKE, FAKE, 1, 0, 0, None) == RC_ERR_STATE
+
+
+def test_scored_write_checks():
+    L = lib()
+    r = fake_ring(100, n_anchor=10, n_memory=30, head=10)
+    need = L.rc_cache_write_scored_workspace_bytes(ctypes.byref(r), 20)
+    assert need >= 8 + 8 * 20 and need % 256 == 0
+    before = state(r)
+
+    def call(n=20, score=FAKE, div=1.0, ws=FAKE, wsb=None):
+        return L.rc_cache_write_scored(ctypes.byref(r), FAKE, FAKE, n, 0, 0, score, div, ws,
+                                       need if wsb is None else wsb, None)
+    assert call(div=0.0) == RC_ERR_ARG
+    assert call(div=1.5) == RC_ERR_ARG
+    assert call(div=float("nan")) == RC_ERR_ARG
+    assert call(score=0) == RC_ERR_ARG
+    assert call(score=FAKE + 2) == RC_ERR_ARG
+    assert call(ws=0) == RC_ERR_ARG
+    assert call(wsb=need - 1) == RC_ERR_ARG
+    assert call(n=61) == RC_ERR_ARG
+    assert state(r) == before
+    big = fake_ring(8000, n_memory=4000)
+    assert L.rc_cache_write_scored(ctypes.byref(big), FAKE, FAKE, 97, 0, 0, FAKE, 1.0, FAKE, 1 << 20,
+                                   None) == RC_ERR_UNSUPPORTED
+    assert "4096" in L.rc_last_error().decode()
+    assert L.rc_cache_write_scored_workspace_bytes(ctypes.byref(fake_ring(100)), 20) == 0   # no memory
+
+
+def test_key_mass_checks():
+    L = lib()
+    r = fake_ring(100, d=128)
+    need = L.rc_key_mass_workspace_bytes(ctypes.byref(r), 70)
+    assert need == 2 * 3 * (272 + 4 * 1024)       # heads x 32-query tiles x record
+    assert L.rc_key_mass_workspace_bytes(ctypes.byref(fake_ring(100, d=64)), 32) == 2 * 1 * (272 + 2 * 1024)
+
+    def call(ring=r, n_q=70, lse=FAKE, mass=FAKE, ws=FAKE, wsb=need, bl=70, scale=0.0):
+        return L.rc_key_mass(ctypes.byref(ring), FAKE, n_q, 0, 0, bl, 0.0, scale, lse, mass, ws, wsb, None)
+    assert call(lse=0) == RC_ERR_ARG
+    assert call(mass=0) == RC_ERR_ARG
+    assert call(n_q=0) == RC_ERR_ARG
+    assert call(bl=0) == RC_ERR_ARG
+    assert call(wsb=need - 16) == RC_ERR_ARG
+    assert call(scale=-1.0) == RC_ERR_ARG
+    assert call(ring=fake_ring(100, kv=RC_BF16)) == RC_ERR_UNSUPPORTED
+    assert L.rc_key_mass_workspace_bytes(ctypes.byref(fake_ring(100, kv=RC_BF16)), 70) == 0

@@ -224,7 +224,7 @@ def test_anchor_argument_checks():
     ring = Ring(10, 1, 2, "f32", 0.0, n_anchor=3)
     with pytest.raises(ValueError):   # a chunk must fit the sliding part
         ring.write(np.zeros((8, 1, 2)), np.zeros((8, 1, 2)), 8, 0, 0)
-    assert ring.state() == (0, 0, 0, 0, 0)
+    assert ring.state() == (0, 0, 0, 0, 0, 0)
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16", "f32"])
