@@ -21,17 +21,20 @@
 //    double-buffered; per tile 2 MFMAs, then exp2(A s + b) summed in the lane.
 // Each mass entry is summed by one lane pair in a fixed order (no atomics).
 //
-// Memory choice (memory_select_kernel, one workgroup) implements the greedy
-// rule of the C ABI in closed form.  Within a block the greedy takes tokens
-// in the order (score desc, slot asc); the k-th of them (rank k) has gain
-// e = Q * gamma^k with gamma^k non-increasing in k, so along each block's
-// list the key (e desc, rank asc, slot asc) increases, and taking the best
-// block head each time is the same as taking the smallest keys overall.  So:
-// sort the candidates by (block, score desc, slot) for the ranks, compute e,
-// sort by (e desc, rank, slot) and keep the first min(M, C).  Scores are
-// float64 sums over heads in head order and gamma^k the float64 product of k
-// factors, as in the rule.  memory_move_kernel then copies the kept tokens of
-// the ring part into the free memory slots.
+// Memory choice implements the greedy rule of the C ABI in closed form.
+// Within a block the greedy takes tokens in the order (score desc, slot asc);
+// the k-th of them (rank k) has gain e = Q * gamma^k with gamma^k
+// non-increasing in k, so along each block's list the key (e desc, rank asc,
+// slot asc) increases, and taking the best block head each time is the same
+// as taking the smallest keys overall.  So a token's rank is the number of
+// its block's tokens before it, its place in the final order the number of
+// tokens with a smaller key, and it is kept when that place is below
+// min(M, candidates): pairwise counts, spread over many workgroups
+// (select_*_kernel), with no sort; gamma^rank is formed once per candidate.
+// Scores are float64 sums over heads in head order and gamma^k the float32
+// product of k factors, as in the rule.
+// memory_move_kernel then copies the kept tokens of the ring part into the
+// free memory slots.
 #include <algorithm>
 #include <cmath>
 
@@ -275,22 +278,143 @@ __global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
 }
 
 // ------------------------------------------------------------ memory choice
-constexpr int kSelThreads = 1024;
-constexpr int kMaxCand = kMaxMemoryCandidates;
+// The list positions c < L = M + n: c < M is memory slot E + c, M + i the
+// i-th slot of the write (head + i, wrapping from E to A); a position is a
+// candidate when its slot holds a token.  Every decision is an integer count
+// over pairs of candidates, added with integer atomics (exact, so the result
+// does not depend on the order in which workgroups run):
+//   rank[c] = candidates of c's block before c in (score desc, slot asc),
+//   pos[c]  = candidates before c in (e desc, rank asc, slot asc),
+//             e = score * gamma^rank;
+// c is kept when pos[c] < K = min(M, candidates).
+constexpr int kSelBlock = 256;  // candidates per workgroup, one per thread
+constexpr int kSelChunk = 64;   // candidates each wave compares against (one per lane)
+constexpr int kMoveRows = 8;    // V^T rows per move workgroup
 
 struct SelArgs {
   const int32_t* slot_block;
   const float* key_score;  // [H][v_ld]
   int H, v_ld;
-  int A, E, N, M;  // anchor end, ring part end (first memory slot), slots, memory slots
-  int head, n_new, rest;  // write range: head .. min(head + n, E) - 1, then A .. A + rest - 1
+  int A, E, M;             // anchor end, ring part end (first memory slot), memory slots
+  int head, n_new, rest;   // the write: head .. min(head + n, E) - 1, then A .. A + rest - 1
+  int L, K;                // M + n; tokens kept, min(M, candidates)
   float gamma;
-  int32_t* moves;  // out: [0] = count, then (src, dst) pairs
+  double* score;           // workspace arrays of L entries
+  double* gain;            // e = score * gamma^rank
+  int32_t* slot;
+  int32_t* blk;            // -1: not a candidate
+  int32_t* rank;
+  int32_t* pos;
 };
 
-// Exclusive prefix sum over the workgroup (every thread passes its value;
-// returns the sum of the values of lower threads; `total` gets the sum).
-__device__ int block_excl_scan(int v, int* sh, int* total) {
+__device__ __forceinline__ int list_slot(const SelArgs& a, int c) {
+  if (c < a.M) return a.E + c;
+  const int i = c - a.M;
+  return a.head + i < a.E ? a.head + i : a.A + (a.head + i - a.E);
+}
+
+// gamma^r as the float32 product of r factors, left to right (a dependent
+// chain of float32 multiplies: far shorter in latency than float64)
+__device__ __forceinline__ float gamma_pow(float g, int r) {
+  if (g == 1.f) return 1.f;
+  float x = 1.f;
+  int i = 0;
+  for (; i + 16 <= r; i += 16) {  // unrolled: one branch per 16 dependent multiplies
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x *= g;
+  }
+  for (; i < r; ++i) x *= g;
+  return x;
+}
+
+// Candidates and their scores (float64 sums over heads, in head order).
+__global__ __launch_bounds__(kSelBlock) void select_score_kernel(SelArgs a) {
+  const int c = blockIdx.x * kSelBlock + threadIdx.x;
+  if (c >= a.L) return;
+  const int s = list_slot(a, c);
+  const int b = a.slot_block[s];
+  double q = 0.0;
+  if (b != -1) {
+    const float* p = a.key_score + s;
+    int h = 0;
+    for (; h + 8 <= a.H; h += 8) {  // eight loads in flight, then the sums in order
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = p[static_cast<size_t>(h + k) * a.v_ld];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q += static_cast<double>(v[k]);
+    }
+    for (; h < a.H; ++h) q += static_cast<double>(p[static_cast<size_t>(h) * a.v_ld]);
+  }
+  a.score[c] = q;
+  a.slot[c] = s;
+  a.blk[c] = b;
+  a.rank[c] = 0;
+  a.pos[c] = 0;
+}
+
+// The chunk's candidates are held one per lane and broadcast with readlane
+// (scalar registers), so the inner loop reads no memory.
+__device__ __forceinline__ int rl(int x, int k) { return __builtin_amdgcn_readlane(x, k); }
+__device__ __forceinline__ double rld(double x, int k) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = rl(static_cast<int>(u & 0xFFFFFFFFu), k), hi = rl(static_cast<int>(u >> 32), k);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// rank[c] += candidates of the chunk in c's block that come before c.
+__global__ __launch_bounds__(kSelBlock) void select_rank_kernel(SelArgs a) {
+  const int lane = threadIdx.x % kWave;
+  const int o = blockIdx.y * kSelChunk + lane;
+  const bool o_in = o < a.L;
+  const double oq = o_in ? a.score[o] : 0.0;
+  const int os = o_in ? a.slot[o] : 0, ob = o_in ? a.blk[o] : -1;
+  const int c = blockIdx.x * kSelBlock + threadIdx.x;
+  const bool in = c < a.L;
+  const int b = in ? a.blk[c] : -1;
+  const double q = in ? a.score[c] : 0.0;
+  const int s = in ? a.slot[c] : 0;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kSelChunk; ++k) {
+    const int kb = rl(ob, k);
+    const double kq = rld(oq, k);
+    const int ks = rl(os, k);
+    cnt += kb == b && (kq > q || (kq == q && ks < s));
+  }
+  if (b != -1 && cnt) atomicAdd(&a.rank[c], cnt);
+}
+
+// e = score * gamma^rank, once per candidate.
+__global__ __launch_bounds__(kSelBlock) void select_gain_kernel(SelArgs a) {
+  const int c = blockIdx.x * kSelBlock + threadIdx.x;
+  if (c >= a.L) return;
+  a.gain[c] = a.blk[c] != -1 ? a.score[c] * static_cast<double>(gamma_pow(a.gamma, a.rank[c])) : 0.0;
+}
+
+// pos[c] += candidates of the chunk that come before c in the final order.
+__global__ __launch_bounds__(kSelBlock) void select_pos_kernel(SelArgs a) {
+  const int lane = threadIdx.x % kWave;
+  const int o = blockIdx.y * kSelChunk + lane;
+  const bool o_in = o < a.L && a.blk[o] != -1;
+  const double oe = o_in ? a.gain[o] : 0.0;
+  const int orank = o_in ? a.rank[o] : 0, os = o_in ? a.slot[o] : 0, ov = o_in;
+  const int c = blockIdx.x * kSelBlock + threadIdx.x;
+  const bool in = c < a.L && a.blk[c] != -1;
+  const double e = in ? a.gain[c] : 0.0;
+  const int r = in ? a.rank[c] : 0, s = in ? a.slot[c] : 0;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kSelChunk; ++k) {
+    const double ke = rld(oe, k);
+    const int kr = rl(orank, k), ks = rl(os, k), kv = rl(ov, k);
+    cnt += kv && (ke > e || (ke == e && (kr < r || (kr == r && ks < s))));
+  }
+  if (in && cnt) atomicAdd(&a.pos[c], cnt);
+}
+
+// Exclusive prefix sum over a 256-thread workgroup; `total` gets the sum.
+__device__ int wg_excl_scan(int v, int* sh, int* total) {
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   int x = v;
 #pragma unroll
@@ -301,7 +425,8 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   if (lane == kWave - 1) sh[w] = x;
   __syncthreads();
   int base = 0, all = 0;
-  for (int i = 0; i < kSelThreads / kWave; ++i) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     const int t = sh[i];
     if (i < w) base += t;
     all += t;
@@ -311,196 +436,96 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void memory_select_kernel(SelArgs a) {
-  __shared__ int32_t c_slot[kMaxCand];
-  __shared__ int32_t c_blk[kMaxCand];
-  __shared__ double c_val[kMaxCand];   // score Q, then e = Q gamma^rank
-  __shared__ double g_pow[kMaxCand];   // gamma^r
-  __shared__ int32_t c_rank[kMaxCand];
-  __shared__ uint16_t order[kMaxCand];
-  __shared__ int32_t flag[kMaxCand];   // per list position, reused
-  __shared__ int sh[kSelThreads / kWave];
-  __shared__ int s_count, s_maxrank;
-  const int tid = threadIdx.x;
-  constexpr int PER = kMaxCand / kSelThreads;  // list positions per thread
-
-  // ---- candidates: occupied memory slots, then occupied slots of the write
-  //      range, compacted in that order
-  const int L = a.M + a.n_new;
-  auto list_slot = [&](int j) {
-    if (j < a.M) return a.E + j;
-    const int i = j - a.M;
-    return a.head + i < a.E ? a.head + i : a.A + (a.head + i - a.E);
-  };
-  int valid[PER], cnt = 0;
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = tid * PER + r;
-    valid[r] = j < L && a.slot_block[list_slot(j)] != -1;
-    cnt += valid[r];
-  }
-  int C;
-  int pos = block_excl_scan(cnt, sh, &C);
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = tid * PER + r;
-    if (valid[r]) {
-      const int s = list_slot(j);
-      c_slot[pos] = s;
-      c_blk[pos] = a.slot_block[s];
-      ++pos;
-    }
-  }
-  __syncthreads();
-  // ---- scores: float64 sums over heads, in head order
-  for (int c = tid; c < C; c += kSelThreads) {
-    const float* p = a.key_score + c_slot[c];
-    double q = 0.0;
-    for (int h = 0; h < a.H; ++h) q += static_cast<double>(p[static_cast<size_t>(h) * a.v_ld]);
-    c_val[c] = q;
-  }
-  int P = 1;
-  while (P < C) P <<= 1;
-  for (int i = tid; i < P; i += kSelThreads) order[i] = static_cast<uint16_t>(i);
-  if (tid == 0) s_maxrank = 0;
-  __syncthreads();
-
-  // bitonic sort of `order` (indices >= C sort last) by the comparator
-  auto bitonic = [&](auto before) {
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P; i += kSelThreads) {
-          const int l = i ^ j;
-          if (l > i) {
-            const int x = order[i], y = order[l];
-            const bool up = (i & k) == 0;
-            const bool y_first = y < C && (x >= C || before(y, x));
-            const bool x_first = x < C && (y >= C || before(x, y));
-            if (up ? y_first : x_first) {
-              order[i] = static_cast<uint16_t>(y);
-              order[l] = static_cast<uint16_t>(x);
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-  };
-  // ---- ranks inside each block: order by (block, score desc, slot)
-  bitonic([&](int x, int y) {
-    if (c_blk[x] != c_blk[y]) return c_blk[x] < c_blk[y];
-    if (c_val[x] != c_val[y]) return c_val[x] > c_val[y];
-    return c_slot[x] < c_slot[y];
-  });
-  for (int p = tid; p < C; p += kSelThreads) {
-    const int b = c_blk[order[p]];
-    int lo = 0, hi = p;  // first position of block b
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (c_blk[order[mid]] < b) lo = mid + 1;
-      else hi = mid;
-    }
-    c_rank[order[p]] = p - lo;
-    atomicMax(&s_maxrank, p - lo);
-  }
-  __syncthreads();
-  if (tid == 0) {  // gamma^r as the float64 product of r factors, in order
-    const double gm = static_cast<double>(a.gamma);
-    double gr = 1.0;
-    for (int r = 0; r <= s_maxrank; ++r) {
-      g_pow[r] = gr;
-      gr *= gm;
-    }
-  }
-  __syncthreads();
-  for (int c = tid; c < C; c += kSelThreads) c_val[c] = c_val[c] * g_pow[c_rank[c]];
-  for (int i = tid; i < P; i += kSelThreads) order[i] = static_cast<uint16_t>(i);
-  __syncthreads();
-  // ---- keep the first min(M, C) by (e desc, rank, slot)
-  bitonic([&](int x, int y) {
-    if (c_val[x] != c_val[y]) return c_val[x] > c_val[y];
-    if (c_rank[x] != c_rank[y]) return c_rank[x] < c_rank[y];
-    return c_slot[x] < c_slot[y];
-  });
-  const int K = min(a.M, C);
-  // flag[j] for memory slot E + j: 1 = holds a kept token; for the write
-  // range in ascending slot order (u < rest: A + u, then head + u - rest):
-  // flag[M + u] = 1 = a kept token to move
-  for (int j = tid; j < L; j += kSelThreads) flag[j] = 0;
-  __syncthreads();
-  for (int p = tid; p < K; p += kSelThreads) {
-    const int s = c_slot[order[p]];
-    if (s >= a.E) flag[s - a.E] = 1;
-    else flag[a.M + (s >= a.head ? a.rest + (s - a.head) : s - a.A)] = 1;
-  }
-  __syncthreads();
-  // free memory slots (no kept token) and incoming tokens, both ascending
-  int f[PER], nf = 0, in[PER], ni = 0;
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = tid * PER + r;
-    f[r] = j < a.M && flag[j] == 0;
-    in[r] = j < a.n_new && flag[a.M + j] == 1;
-    nf += f[r];
-    ni += in[r];
-  }
-  int n_free, n_in;
-  int fpos = block_excl_scan(nf, sh, &n_free);
-  int ipos = block_excl_scan(ni, sh, &n_in);
-  // the k-th incoming token goes to the k-th free slot; the free slots are
-  // staged in c_slot (the candidate data is no longer needed)
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = tid * PER + r;
-    if (f[r]) c_slot[fpos++] = a.E + j;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int u = tid * PER + r;
-    if (in[r]) {
-      const int s = u < a.rest ? a.A + u : a.head + (u - a.rest);
-      a.moves[2 + 2 * ipos] = s;
-      a.moves[3 + 2 * ipos] = c_slot[ipos];
-      ++ipos;
-    }
-  }
-  if (tid == 0) a.moves[0] = n_in;
-}
-
-// Copy kept tokens (K row, V^T column, scales, position, block) from the ring
-// part to their memory slots: workgroup h handles head h.
+// Workgroup (h, group): every workgroup pairs the k-th kept token of the
+// ring part (ascending slot) with the k-th memory slot that holds no kept
+// token (ascending), then copies its share for head h: V^T rows
+// group*8 .. +7, a share of the K rows, and (group 0) the scales and (head 0)
+// positions and blocks.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void memory_move_kernel(RingView r, const int32_t* moves) {
-  const int h = blockIdx.x;
-  const int count = moves[0];
+__global__ __launch_bounds__(256) void memory_move_kernel(RingView r, SelArgs a) {
+  __shared__ int32_t src_s[kMaxMemoryCandidates];
+  __shared__ int32_t dst_s[kMaxMemoryCandidates];
+  __shared__ int sh[4];
+  constexpr int G = D / kMoveRows;
+  const int h = blockIdx.x / G, grp = blockIdx.x % G;
   const int tid = threadIdx.x;
+  auto kept = [&](int c) { return a.blk[c] != -1 && a.pos[c] < a.K; };
+  int n_free = 0, n_in = 0;
+  for (int base = 0; base < a.M; base += 256) {
+    const int j = base + tid;
+    const int f = j < a.M && !kept(j);
+    int tot;
+    const int at = wg_excl_scan(f, sh, &tot);
+    if (f) dst_s[n_free + at] = a.E + j;
+    n_free += tot;
+  }
+  for (int base = 0; base < a.n_new; base += 256) {
+    const int u = base + tid;  // ascending slots: the wrapped part A.., then head..
+    int f = 0, s = 0;
+    if (u < a.n_new) {
+      const int i = u < a.rest ? (a.E - a.head) + u : u - a.rest;
+      s = u < a.rest ? a.A + u : a.head + (u - a.rest);
+      f = kept(a.M + i);
+    }
+    int tot;
+    const int at = wg_excl_scan(f, sh, &tot);
+    if (f) src_s[n_in + at] = s;
+    n_in += tot;
+  }
+  __syncthreads();
+  const int pairs = min(n_in, n_free);
   uint8_t* k = static_cast<uint8_t*>(r.k) + static_cast<size_t>(h) * r.v_ld * D * ES;
   uint8_t* v = static_cast<uint8_t*>(r.v) + static_cast<size_t>(h) * D * r.v_ld * ES;
-  constexpr int kPieces = D * ES / 16;  // 16-byte pieces per K row
-  for (int i = tid; i < count * kPieces; i += 256) {
-    const int m = i / kPieces, pc = i % kPieces;
-    const int src = moves[2 + 2 * m], dst = moves[3 + 2 * m];
-    *reinterpret_cast<v4u*>(k + static_cast<size_t>(dst) * D * ES + pc * 16) =
-        *reinterpret_cast<const v4u*>(k + static_cast<size_t>(src) * D * ES + pc * 16);
-  }
-  for (int i = tid; i < count * D; i += 256) {
-    const int m = i / D, j = i % D;
-    const int src = moves[2 + 2 * m], dst = moves[3 + 2 * m];
-    uint8_t* row = v + static_cast<size_t>(j) * r.v_ld * ES;
-    if constexpr (ES == 1) row[dst] = row[src];
-    else if constexpr (ES == 2) reinterpret_cast<uint16_t*>(row)[dst] = reinterpret_cast<const uint16_t*>(row)[src];
-    else reinterpret_cast<uint32_t*>(row)[dst] = reinterpret_cast<const uint32_t*>(row)[src];
-  }
-  for (int m = tid; m < count; m += 256) {
-    const int src = moves[2 + 2 * m], dst = moves[3 + 2 * m];
-    if (r.k_scale) {
-      r.k_scale[static_cast<size_t>(h) * r.v_ld + dst] = r.k_scale[static_cast<size_t>(h) * r.v_ld + src];
-      r.v_scale[static_cast<size_t>(h) * r.v_ld + dst] = r.v_scale[static_cast<size_t>(h) * r.v_ld + src];
+  // V^T: rows grp*8 .. +7 of every pair, loads first
+  for (int m = tid; m < pairs; m += 256) {
+    const int src = src_s[m], dst = dst_s[m];
+    uint32_t x[kMoveRows];
+#pragma unroll
+    for (int j = 0; j < kMoveRows; ++j) {
+      const uint8_t* row = v + static_cast<size_t>(grp * kMoveRows + j) * r.v_ld * ES;
+      if constexpr (ES == 1) x[j] = row[src];
+      else if constexpr (ES == 2) x[j] = reinterpret_cast<const uint16_t*>(row)[src];
+      else x[j] = reinterpret_cast<const uint32_t*>(row)[src];
     }
-    if (h == 0) {
-      r.slot_pos[dst] = r.slot_pos[src];
-      r.slot_block[dst] = r.slot_block[src];
+#pragma unroll
+    for (int j = 0; j < kMoveRows; ++j) {
+      uint8_t* row = v + static_cast<size_t>(grp * kMoveRows + j) * r.v_ld * ES;
+      if constexpr (ES == 1) row[dst] = static_cast<uint8_t>(x[j]);
+      else if constexpr (ES == 2) reinterpret_cast<uint16_t*>(row)[dst] = static_cast<uint16_t>(x[j]);
+      else reinterpret_cast<uint32_t*>(row)[dst] = x[j];
+    }
+  }
+  // K rows: 16-byte pieces, spread over the G workgroups of the head
+  constexpr int KP = D * ES / 16;
+  for (int i0 = grp * 256 + tid; i0 < pairs * KP; i0 += 4 * G * 256) {
+    v4u x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * G * 256;
+      if (i < pairs * KP)
+        x[u] = *reinterpret_cast<const v4u*>(k + static_cast<size_t>(src_s[i / KP]) * D * ES + (i % KP) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * G * 256;
+      if (i < pairs * KP)
+        *reinterpret_cast<v4u*>(k + static_cast<size_t>(dst_s[i / KP]) * D * ES + (i % KP) * 16) = x[u];
+    }
+  }
+  if (grp == 0) {
+    for (int m = tid; m < pairs; m += 256) {
+      const int src = src_s[m], dst = dst_s[m];
+      if (r.k_scale) {
+        const size_t o = static_cast<size_t>(h) * r.v_ld;
+        const float ks = r.k_scale[o + src], vs = r.v_scale[o + src];
+        r.k_scale[o + dst] = ks;
+        r.v_scale[o + dst] = vs;
+      }
+      if (h == 0) {
+        const int p = r.slot_pos[src], b = r.slot_block[src];
+        r.slot_pos[dst] = p;
+        r.slot_block[dst] = b;
+      }
     }
   }
 }
@@ -557,37 +582,47 @@ hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* ls
 
 size_t memory_workspace_bytes(int n_memory, int n_new) {
   if (n_memory <= 0) return 0;
-  const size_t pairs = static_cast<size_t>(std::min(n_memory, n_new));
-  return (8 + 8 * pairs + 255) / 256 * 256;
+  const size_t L = static_cast<size_t>(n_memory) + n_new;
+  return (L * (2 * 8 + 4 * 4) + 255) / 256 * 256;
 }
 
 hipError_t launch_memory_update(const RingView& r, const float* key_score, float gamma, int head, int n_new,
-                                void* workspace, hipStream_t s) {
+                                int n_candidates, void* workspace, hipStream_t s) {
   SelArgs a{};
   a.slot_block = r.slot_block;
   a.key_score = key_score;
   a.H = r.H;
   a.v_ld = r.v_ld;
   a.A = r.n_anchor;
-  a.N = r.N;
   a.M = r.n_memory;
   a.E = r.N - r.n_memory;
   a.head = head;
   a.n_new = n_new;
   a.rest = std::max(0, head + n_new - a.E);
+  a.L = a.M + n_new;
+  a.K = std::min(a.M, n_candidates);
   a.gamma = gamma;
-  a.moves = static_cast<int32_t*>(workspace);
-  hipLaunchKernelGGL(memory_select_kernel, dim3(1), dim3(kSelThreads), 0, s, a);
+  a.score = static_cast<double*>(workspace);
+  a.gain = a.score + a.L;
+  a.slot = reinterpret_cast<int32_t*>(a.gain + a.L);
+  a.blk = a.slot + a.L;
+  a.rank = a.blk + a.L;
+  a.pos = a.rank + a.L;
+  const int nb = (a.L + kSelBlock - 1) / kSelBlock, nc = (a.L + kSelChunk - 1) / kSelChunk;
+  hipLaunchKernelGGL(select_score_kernel, dim3(nb), dim3(kSelBlock), 0, s, a);
+  hipLaunchKernelGGL(select_rank_kernel, dim3(nb, nc), dim3(kSelBlock), 0, s, a);
+  hipLaunchKernelGGL(select_gain_kernel, dim3(nb), dim3(kSelBlock), 0, s, a);
+  hipLaunchKernelGGL(select_pos_kernel, dim3(nb, nc), dim3(kSelBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int32_t* mv = a.moves;
+  const dim3 grid(r.H * (r.d / kMoveRows));
   switch (r.kv * 1000 + r.d) {
-    case KV_FP8 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<1, 128>), dim3(r.H), dim3(256), 0, s, r, mv); break;
-    case KV_FP8 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<1, 64>), dim3(r.H), dim3(256), 0, s, r, mv); break;
-    case KV_BF16 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<2, 128>), dim3(r.H), dim3(256), 0, s, r, mv); break;
-    case KV_BF16 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<2, 64>), dim3(r.H), dim3(256), 0, s, r, mv); break;
-    case KV_F32 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<4, 128>), dim3(r.H), dim3(256), 0, s, r, mv); break;
-    case KV_F32 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<4, 64>), dim3(r.H), dim3(256), 0, s, r, mv); break;
+    case KV_FP8 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<1, 128>), grid, dim3(256), 0, s, r, a); break;
+    case KV_FP8 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<1, 64>), grid, dim3(256), 0, s, r, a); break;
+    case KV_BF16 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<2, 128>), grid, dim3(256), 0, s, r, a); break;
+    case KV_BF16 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<2, 64>), grid, dim3(256), 0, s, r, a); break;
+    case KV_F32 * 1000 + 128: hipLaunchKernelGGL((memory_move_kernel<4, 128>), grid, dim3(256), 0, s, r, a); break;
+    case KV_F32 * 1000 + 64: hipLaunchKernelGGL((memory_move_kernel<4, 64>), grid, dim3(256), 0, s, r, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

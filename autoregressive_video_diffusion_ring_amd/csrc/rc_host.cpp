@@ -240,8 +240,8 @@ rc_status rc_cache_write_scored(rc_ring* r, const void* k_new, const void* v_new
     if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(RC_ERR_ARG, "workspace must be 16-byte aligned");
   }
   if (update) {
-    hipError_t e = rc::launch_memory_update(view(r), key_score, diversity, r->head, n_new, workspace,
-                                            as_stream(stream));
+    hipError_t e = rc::launch_memory_update(view(r), key_score, diversity, r->head, n_new, r->n_mem + evicted,
+                                            workspace, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "memory update");
   }
   st = do_write(r, k_new, v_new, n_new, pos0, block_id, as_stream(stream));

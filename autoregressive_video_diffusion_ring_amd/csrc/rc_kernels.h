@@ -62,7 +62,7 @@ hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* ls
 constexpr int kMaxMemoryCandidates = 4096;
 size_t memory_workspace_bytes(int n_memory, int n_new);
 hipError_t launch_memory_update(const RingView& r, const float* key_score, float gamma, int head, int n_new,
-                                void* workspace, hipStream_t s);
+                                int n_candidates, void* workspace, hipStream_t s);
 
 hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
                                    uint8_t* mask, hipStream_t s);

@@ -28,7 +28,11 @@ ten blocks' queries.
 reset every 300 chunks by a delta rotation of all 60 rings, ten cache-bias
 ramps 0, -2, -4, -2, 0) and prints one JSON line with the sustained ms/chunk
 (median and p99).  ``--anchor A`` makes those rings anchored: the first A
-tokens (A = 757: the first chunk) stay pinned and the other slots slide.
+tokens (A = 757: the first chunk) stay pinned and the other slots slide;
+``--memory M`` adds a scored content memory of M slots: the last pass of
+every chunk also computes each layer's key mass (rc_key_mass, from that
+pass's queries and lse), and the next chunk's first write keeps the best
+tokens in the memory (rc_cache_write_scored, diversity ``--diversity``).
 """
 from __future__ import annotations
 
@@ -183,27 +187,39 @@ def bias_at(t: int) -> float:
     return 0.0
 
 
-def longrun(n_chunks: int, anchor: int = 0) -> dict:
+def longrun(n_chunks: int, anchor: int = 0, memory: int = 0, diversity: float = 0.9) -> dict:
     """Sustained chunks of the long-run schedule from an empty cache: each
     chunk is 4 passes x 60 layers of write + attention, then 60 advances;
     before every 300th chunk all 60 rings are rerotated so that the most
     recent N cached positions become 0..N-1 (the oldest cached position of a
     plain ring; an anchor, older still, moves below 0 with them); the cache
     bias follows ten ramps.  With anchor > 0 every ring pins its first
-    `anchor` tokens."""
+    `anchor` tokens; with memory > 0 every ring has a scored content memory
+    of that many slots, scored by the key mass of each chunk's last pass."""
     import torch
 
-    from autoregressive_video_diffusion_ring_amd import Ring, rc_cache_write, rc_chunk_attention, rc_ring_advance
+    from autoregressive_video_diffusion_ring_amd import (Ring, rc_cache_write, rc_cache_write_scored,
+                                                         rc_cache_write_scored_workspace_bytes, rc_chunk_attention,
+                                                         rc_key_mass, rc_key_mass_workspace_bytes, rc_ring_advance)
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     gen = torch.Generator(device=dev)
     gen.manual_seed(4)
-    rings = [Ring(N, H, D, "fp8", 10000.0, n_anchor=anchor, device=dev) for _ in range(LAYERS)]
+    rings = [Ring(N, H, D, "fp8", 10000.0, n_anchor=anchor, n_memory=memory, device=dev) for _ in range(LAYERS)]
     pool = [[torch.randn((NEW, H, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
              for _ in range(3)] for _ in range(POOL)]
     out = torch.empty((NEW, H, D), dtype=torch.bfloat16, device=dev)
     structs = [r.struct for r in rings]
+    if memory:
+        v_ld = rings[0].v_ld
+        masses = torch.zeros((LAYERS, H, v_ld), dtype=torch.float32, device=dev)
+        lse = torch.empty((H, NEW), dtype=torch.float32, device=dev)
+        nb_m = rc_key_mass_workspace_bytes(structs[0], NEW)
+        ws_m = torch.empty(nb_m, dtype=torch.uint8, device=dev)
+        nb_w = rc_cache_write_scored_workspace_bytes(structs[0], NEW)
+        ws_w = torch.empty(nb_w, dtype=torch.uint8, device=dev)
+    ev_mass, ev_scored = [], []
     torch.cuda.synchronize()
     evs, resets = [], []
     for t in range(n_chunks):
@@ -216,10 +232,34 @@ def longrun(n_chunks: int, anchor: int = 0) -> dict:
             resets.append(t)
         pos0, bias = chunk_pos0(t), bias_at(t)
         for p in range(PASSES):
+            score = memory and p == PASSES - 1
+            if score:
+                masses.zero_()
             for layer in range(LAYERS):
                 q, k, v = pool[(240 * t + 60 * p + layer) % POOL]
-                rc_cache_write(structs[layer], k, v, NEW, pos0, t, sptr)
-                rc_chunk_attention(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, out, None, None, 0, sptr)
+                sample = layer == 0 and t >= 8
+                if memory and p == 0:
+                    if sample:
+                        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        a0.record(stream)
+                    rc_cache_write_scored(structs[layer], k, v, NEW, pos0, t, masses[layer], diversity, ws_w, nb_w,
+                                          sptr)
+                    if sample:
+                        a1.record(stream)
+                        ev_scored.append((a0, a1))
+                else:
+                    rc_cache_write(structs[layer], k, v, NEW, pos0, t, sptr)
+                rc_chunk_attention(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, out, lse if score else None,
+                                   None, 0, sptr)
+                if score:
+                    if sample:
+                        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        b0.record(stream)
+                    rc_key_mass(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, lse, masses[layer], ws_m, nb_m,
+                                sptr)
+                    if sample:
+                        b1.record(stream)
+                        ev_mass.append((b0, b1))
         for s in structs:
             rc_ring_advance(s, NEW)
         e1.record(stream)
@@ -233,9 +273,13 @@ def longrun(n_chunks: int, anchor: int = 0) -> dict:
     full = sorted(ms[8:])
     pick = lambda v, f: v[min(len(v) - 1, int(f * len(v)))]
     kind = f"anchored fp8 ring, first {anchor} tokens pinned" if anchor else "fp8 ring"
+    if memory:
+        kind += f", scored memory of {memory} slots (diversity {diversity})"
+    med = lambda evl: (sorted(a.elapsed_time(b) for a, b in evl)[len(evl) // 2] * 1e3) if evl else None
     return {"metric": f"sustained ms/chunk, long-run schedule (757 new x 5788-slot {kind}, 60 layers)",
             "value": round(pick(full, 0.5), 4), "unit": "ms", "higher_is_better": False,
-            "n_anchor": anchor, "final_head": rings[0].state()[0],
+            "n_anchor": anchor, "n_memory": memory, "final_state": list(rings[0].state()),
+            "key_mass_us": med(ev_mass), "scored_write_us": med(ev_scored),
             "chunks": n_chunks, "p99_ms": round(pick(full, 0.99), 4), "mean_ms": round(sum(full) / len(full), 4),
             "steady_median_ms": round(pick(steady, 0.5), 4),
             "reset_chunk_ms": [round(ms[i], 3) for i in resets],
@@ -279,6 +323,9 @@ def main() -> int:
                     help="run K chunks of the long-run schedule instead and print that line")
     ap.add_argument("--anchor", type=int, default=0, metavar="A",
                     help="with --longrun: pin the first A tokens of every ring (757 = the first chunk)")
+    ap.add_argument("--memory", type=int, default=0, metavar="M",
+                    help="with --longrun: a scored content memory of M slots in every ring")
+    ap.add_argument("--diversity", type=float, default=0.9, help="with --memory: gamma in (0, 1]")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -293,7 +340,7 @@ def main() -> int:
 
     if args.longrun > 0:
         torch.cuda.set_device(0)
-        print(json.dumps(longrun(args.longrun, args.anchor)), flush=True)
+        print(json.dumps(longrun(args.longrun, args.anchor, args.memory, args.diversity)), flush=True)
         return 0
 
     dev = torch.device("cuda", 0)

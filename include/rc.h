@@ -233,9 +233,10 @@ size_t rc_key_mass_workspace_bytes(const rc_ring* ring, int32_t n_q);
  *              spreads the memory over more blocks.  The choice is the greedy
  *              one: each block offers its best remaining token (higher Q,
  *              then lower slot) with gain Q gamma^c (c tokens of the block
- *              already kept; gamma^c the float64 product of c factors of the
- *              float32 gamma); the largest gain is kept, ties to the smaller
- *              c, then the lower slot.
+ *              already kept; gamma^c the float32 product of c factors of the
+ *              float32 gamma, left to right; the gain is the float64
+ *              product); the largest gain is kept, ties to the smaller c, then
+ *              the lower slot.
  *   workspace  device scratch of rc_cache_write_scored_workspace_bytes(ring,
  *              n_new) bytes
  * Kept tokens from the sliding part move (K, V, scales, position, block) into

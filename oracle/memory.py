@@ -32,9 +32,12 @@ objective is separable and concave per block, so the greedy picks are an
 optimal set (the tests check this against brute force over all subsets on
 small cases).  Precision fixed so that the choice is reproducible: Q_s is
 the float64 sum of the float32 per-head scores in head order 0..H-1;
-gamma^c is the float64 product gamma * gamma * ... (c factors, left to
-right), gamma^0 = 1, gamma the float32 value given.  Scores are finite and
-non-negative (attention mass is).
+gamma^c is the float32 product gamma * gamma * ... (c factors, left to
+right, each product rounded to float32), gamma^0 = 1, gamma the float32
+value given; the gain is the float64 product of Q_s and gamma^c.  A float32
+chain never increases with c (each rounding is monotone), which keeps every
+block's gains in order.  Scores are finite and non-negative (attention mass
+is).
 """
 from __future__ import annotations
 
@@ -84,12 +87,13 @@ def slot_score(key_score: np.ndarray, s: int) -> float:
 
 
 def gamma_power(gamma: float, c: int) -> float:
-    """gamma^c as the float64 product of c factors, left to right."""
-    g = float(np.float32(gamma))
-    r = 1.0
+    """gamma^c as the float32 product of c factors, left to right (returned
+    as the exact float64 value of that float32)."""
+    g = np.float32(gamma)
+    r = np.float32(1.0)
     for _ in range(c):
-        r *= g
-    return r
+        r = np.float32(r * g)
+    return float(r)
 
 
 def select_memory(candidates, slot_block, key_score, M: int, gamma: float) -> list[int]:
