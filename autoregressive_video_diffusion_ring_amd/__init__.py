@@ -18,13 +18,14 @@ import ctypes
 
 import torch
 
-from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RcError, RcRing, check, lib)
+from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, RC_MASK_SAME_BLOCK, RcError, RcRing,
+                   check, lib)
 
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
     "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_workspace_bytes", "rc_cache_write_scored",
-    "rc_cache_write_scored_workspace_bytes",
+    "rc_cache_write_scored_workspace_bytes", "rc_chunk_attention_ex", "RC_MASK_BLOCK_CAUSAL", "RC_MASK_SAME_BLOCK",
 ]
 
 
@@ -87,6 +88,14 @@ def rc_chunk_attention(ring: RcRing, q, n_q: int, q_pos0: int, q_block0: int, q_
     check(lib().rc_chunk_attention(ctypes.byref(ring), _ptr(q), n_q, q_pos0, q_block0, q_block_len,
                                    float(cache_bias), float(softmax_scale), _ptr(out), _ptr(lse),
                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rc_chunk_attention_ex(ring: RcRing, q, n_q: int, q_pos0: int, q_block, q_block0: int, q_block_len: int,
+                          mask: int, cache_bias: float, softmax_scale: float, out, lse=None, workspace=None,
+                          workspace_bytes: int = 0, stream=None) -> None:
+    check(lib().rc_chunk_attention_ex(ctypes.byref(ring), _ptr(q), n_q, q_pos0, _ptr(q_block), q_block0,
+                                      q_block_len, mask, float(cache_bias), float(softmax_scale), _ptr(out),
+                                      _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def rc_attention_workspace_bytes(ring: RcRing, n_q: int) -> int:
@@ -212,7 +221,9 @@ class Ring:
 
     def attention(self, q, q_pos0: int, q_block0: int, q_block_len: int | None = None,
                   cache_bias: float = 0.0, softmax_scale: float = 0.0, out=None, lse=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, q_block=None, same_block: bool = False):
+        """q_block: optional int32 [n_q] device tensor of per-query blocks;
+        same_block: the text cross-attention mask (slot block == query block)."""
         n_q = q.shape[0]
         shape = (n_q, self.H, self.d)
         _check_tensor(q, "q", self.input_dtype, shape, self.device)
@@ -228,8 +239,15 @@ class Ring:
                 workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         if workspace is not None:
             ws_bytes = workspace.numel() * workspace.element_size()
-        rc_chunk_attention(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias,
-                           softmax_scale, out, lse, workspace, ws_bytes, stream)
+        if q_block is None and not same_block:
+            rc_chunk_attention(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias,
+                               softmax_scale, out, lse, workspace, ws_bytes, stream)
+        else:
+            if q_block is not None:
+                _check_tensor(q_block, "q_block", torch.int32, (n_q,), self.device)
+            rc_chunk_attention_ex(self.struct, q, n_q, q_pos0, q_block, q_block0, q_block_len or n_q,
+                                  RC_MASK_SAME_BLOCK if same_block else RC_MASK_BLOCK_CAUSAL, cache_bias,
+                                  softmax_scale, out, lse, workspace, ws_bytes, stream)
         return out
 
     def visibility(self, n_q: int, q_block0: int, q_block_len: int, stream=None):

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librc.so")
 
 RC_OK, RC_ERR_ARG, RC_ERR_UNSUPPORTED, RC_ERR_STATE, RC_ERR_HIP = range(5)
 RC_F32, RC_BF16, RC_FP8_E4M3 = range(3)
+RC_MASK_BLOCK_CAUSAL, RC_MASK_SAME_BLOCK = range(2)
 STATUS_NAMES = {0: "RC_OK", 1: "RC_ERR_ARG", 2: "RC_ERR_UNSUPPORTED", 3: "RC_ERR_STATE", 4: "RC_ERR_HIP"}
 DTYPES = {"f32": RC_F32, "bf16": RC_BF16, "fp8": RC_FP8_E4M3}
 
@@ -47,6 +48,8 @@ SIGNATURES = {
     "rc_cache_rerotate": (c_int32, [POINTER(RcRing), c_int32, c_void_p]),
     "rc_chunk_attention": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "rc_chunk_attention_ex": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                        c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "rc_attention_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
     "rc_ring_advance": (c_int32, [POINTER(RcRing), c_int32]),
     "rc_key_mass": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,

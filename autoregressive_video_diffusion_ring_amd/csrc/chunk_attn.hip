@@ -96,6 +96,8 @@ struct AttnArgs {
   int n_items;  // workgroups launched
   int use_rope;
   RopeTable rope;
+  const int32_t* q_block_ids;  // [n_q] block per query, or null: q_block0 + i / q_block_len
+  int same_block;              // mask: visible iff slot block == query block (no bias)
 };
 
 // LDS geometry of one tile buffer (K rows, then V^T rows).
@@ -307,7 +309,9 @@ __device__ __forceinline__ int wave_minmax_i32(int v) {
   return op(static_cast<int>(r32[0]), static_cast<int>(r32[1]));
 }
 
-template <int KV, int D>
+// GEN: per-query block ids and the same-block mask (rc_chunk_attention_ex);
+// without it the kernel is the plain block-causal one.
+template <int KV, int D, bool GEN>
 __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   using T = Tile<KV, D>;
   constexpr int KPS = Stages<KV, D>::kps;
@@ -378,9 +382,16 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
   const int wave_q0 = q_base + wq * kQW;
   const bool wave_active = wave_q0 < a.n_q;
   const int wave_q1 = max(min(wave_q0 + kQW, a.n_q) - 1, wave_q0);
-  const int qb_lo = a.q_block0 + wave_q0 / a.q_block_len;
-  const int qb_hi = a.q_block0 + wave_q1 / a.q_block_len;
-  const int my_qb = a.q_block0 + (q_ok ? qi : wave_q0) / a.q_block_len;
+  int qb_lo = a.q_block0 + wave_q0 / a.q_block_len;
+  int qb_hi = a.q_block0 + wave_q1 / a.q_block_len;
+  int my_qb = a.q_block0 + (q_ok ? qi : wave_q0) / a.q_block_len;
+  if (GEN && a.q_block_ids) {  // explicit blocks: the wave's range from a reduction
+    my_qb = a.q_block_ids[q_ok ? qi : min(wave_q0, a.n_q - 1)];
+    qb_lo = __builtin_amdgcn_readfirstlane(wave_minmax_i32<false>(my_qb));
+    qb_hi = __builtin_amdgcn_readfirstlane(wave_minmax_i32<true>(my_qb));
+  }
+  const bool same_block = GEN && a.same_block != 0;
+  const int lo_qb = same_block ? my_qb : 0;  // lowest visible block (empty slots hold -1)
 
   // ---- slot metadata for the factor tables.  Wave f = wq of key half 0
   //      builds table f (tile f % KPS of half f / KPS) of every step, from
@@ -549,10 +560,16 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
     const int all = __builtin_amdgcn_readfirstlane(sm.y);
     const int kmin = __builtin_amdgcn_readfirstlane(sm.z);
     const int kmax = __builtin_amdgcn_readfirstlane(sm.w);
+    const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
+    if (GEN && same_block) {  // slots of the query's own block only, never biased
+      vis = any && kmin <= qb_hi && kmax >= qb_lo;
+      fast = all_same;
+      hist = false;
+      return;
+    }
     vis = any && kmin <= qb_hi;
     const bool all_vis = all && kmax <= qb_lo;
     const bool all_hist = all && kmax < qb_lo;
-    const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
     fast = all_vis && (all_hist || all_same || a.bias_log2 == 0.f);
     hist = fast && all_hist;
   };
@@ -624,7 +641,11 @@ __global__ __launch_bounds__(kThreads) void chunk_attn_kernel(AttnArgs a) {
           const int kba[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int cls = visibility_class(kba[r], my_qb);
+            // visible iff lo_qb <= block <= my_qb (lo_qb = 0, or the query's
+            // own block for the same-block mask, whose bias is zero)
+            const int kb = kba[r];
+            const int cls = !GEN ? visibility_class(kb, my_qb)
+                                 : (kb < lo_qb || kb > my_qb) ? kVisNone : (kb < my_qb ? kVisBias : kVisPlain);
             float z = fmaf(s[mb][4 * qq + r], afa[r], negm);
             z = cls == kVisBias ? z + a.bias_log2 : z;
             s[mb][4 * qq + r] = cls == kVisNone ? -INFINITY : z;
@@ -905,9 +926,11 @@ hipError_t attn_impl(const RingView& r, const AttnCall& c, int splits, hipStream
   a.q_pos0 = c.q_pos0;
   a.q_block0 = c.q_block0;
   a.q_block_len = c.q_block_len;
+  a.q_block_ids = c.q_block_ids;
+  a.same_block = c.same_block;
   const float sigma = c.softmax_scale != 0.f ? c.softmax_scale : 1.f / std::sqrt(static_cast<float>(r.d));
   a.scale_log2 = sigma * kLog2e;
-  a.bias_log2 = c.cache_bias * kLog2e;
+  a.bias_log2 = c.same_block ? 0.f : c.cache_bias * kLog2e;  // the same-block mask has no earlier blocks
   a.out = c.out;
   a.lse = c.lse;
   a.n_qt = (c.n_q + kQT - 1) / kQT;
@@ -924,7 +947,10 @@ hipError_t attn_impl(const RingView& r, const AttnCall& c, int splits, hipStream
   const int total = a.n_qt * r.H * splits;
   a.remap = (total % 8 == 0) ? 1 : 0;
   a.n_items = total;
-  hipLaunchKernelGGL((chunk_attn_kernel<KV, D>), dim3(total), dim3(kThreads), 0, s, a);
+  if (a.q_block_ids || a.same_block)
+    hipLaunchKernelGGL((chunk_attn_kernel<KV, D, true>), dim3(total), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_attn_kernel<KV, D, false>), dim3(total), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int rows = c.n_q * r.H;

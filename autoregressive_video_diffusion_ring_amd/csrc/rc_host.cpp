@@ -268,9 +268,10 @@ size_t rc_attention_workspace_bytes(const rc_ring* r, int32_t n_q) {
   return rc::attention_workspace_bytes(view(r), n_q);
 }
 
-rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
-                             int32_t q_block_len, float cache_bias, float softmax_scale, void* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+rc_status rc_chunk_attention_ex(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, const int32_t* q_block,
+                                int32_t q_block0, int32_t q_block_len, int32_t mask, float cache_bias,
+                                float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   rc_status st = check_ring(r);
   if (st != RC_OK) return st;
   if (!rc::attention_supported(r->kv_dtype, r->head_dim))
@@ -279,18 +280,29 @@ rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15u)
     return fail(RC_ERR_ARG, "q and out must be 16-byte aligned");
   if (n_q < 1) return fail(RC_ERR_ARG, "n_q must be >= 1 (got %d)", n_q);
-  if (q_block_len < 1) return fail(RC_ERR_ARG, "q_block_len must be >= 1 (got %d)", q_block_len);
+  if (!q_block && q_block_len < 1) return fail(RC_ERR_ARG, "q_block_len must be >= 1 (got %d)", q_block_len);
+  if (q_block && (reinterpret_cast<uintptr_t>(q_block) & 3u)) return fail(RC_ERR_ARG, "q_block must be 4-byte aligned");
+  if (mask != RC_MASK_BLOCK_CAUSAL && mask != RC_MASK_SAME_BLOCK) return fail(RC_ERR_ARG, "unknown mask %d", mask);
   if (static_cast<long long>(q_pos0) + n_q - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
   if (!std::isfinite(cache_bias) && !(cache_bias < 0.f))
     return fail(RC_ERR_ARG, "cache_bias must be finite or -inf");
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
     return fail(RC_ERR_ARG, "softmax_scale must be finite and >= 0");
   if (workspace_bytes > 0 && !workspace) return fail(RC_ERR_ARG, "workspace_bytes > 0 with a NULL workspace");
-  rc::AttnCall c{q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, out, lse, workspace,
+  rc::AttnCall c{q, n_q, q_pos0, q_block0, q_block ? 1 : q_block_len, cache_bias, softmax_scale, out, lse, workspace,
                  workspace_bytes};
+  c.q_block_ids = q_block;
+  c.same_block = mask == RC_MASK_SAME_BLOCK;
   hipError_t e = rc::launch_chunk_attention(view(r), c, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk attention");
   return ok();
+}
+
+rc_status rc_chunk_attention(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                             int32_t q_block_len, float cache_bias, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return rc_chunk_attention_ex(r, q, n_q, q_pos0, nullptr, q_block0, q_block_len, RC_MASK_BLOCK_CAUSAL, cache_bias,
+                               softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t rc_key_mass_workspace_bytes(const rc_ring* r, int32_t n_q) {

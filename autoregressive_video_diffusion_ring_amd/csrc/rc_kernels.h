@@ -41,6 +41,8 @@ struct AttnCall {
   float* lse;
   void* workspace;
   size_t workspace_bytes;
+  const int32_t* q_block_ids = nullptr;  // [n_q] or null (q_block0 + i / q_block_len)
+  int same_block = 0;                    // 1: visible iff slot block == query block
 };
 
 // Whether an attention kernel is built for this KV format and head size.

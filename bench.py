@@ -19,10 +19,12 @@ chunks; the write and rerotate kernels' bandwidths are reported beside it.
 recorded rocprofv3 counter runs, or null if the kernel changed since.
 ``cpu_baseline`` times the float64 oracle on the host cores on a bounded sample
 of the same workload (layer calls, about ten seconds).  ``joint_av`` times the
-four paths of a joint audio-video block (StreamLTX project page, Training:
+six paths of a joint audio-video block (StreamLTX project page, Training:
 one-second blocks of 1,152 video and 25 audio tokens, 10 blocks cached, 32
-heads, bf16, block-causal), each with the last block's queries and with all
-ten blocks' queries.
+heads, bf16, block-causal; Data: each block sees only its own segment's
+prompt, here three prompts of 96-160 tokens), each with the last block's
+queries and with all ten blocks' queries, and video self-attention with the
+first block one latent frame longer (1,536 tokens).
 
 ``--longrun K`` instead runs K chunks of the long-run schedule (a position
 reset every 300 chunks by a delta rotation of all 60 rings, ten cache-bias
@@ -150,6 +152,53 @@ def joint_av(dev, stream) -> dict:
         rings[name] = (r, blen)
         qs[name] = rnd(blen * AV_BLOCKS)
     res = {}
+    # text cross-attention: three prompt segments (blocks 0-3, 4-6, 7-9; 128,
+    # 96 and 160 tokens), each block sees only its own segment's prompt
+    seg_of_block = [0, 0, 0, 0, 1, 1, 1, 2, 2, 2]
+    prompts = [128, 96, 160]
+    text = Ring(sum(prompts), AV_H, D, "bf16", 0.0, device=dev)
+    for sg, n in enumerate(prompts):
+        text.write(rnd(n), rnd(n), 0, sg)
+        if sg < len(prompts) - 1:
+            text.advance(n)
+    for qn in ("video", "audio"):
+        qblen = rings[qn][1]
+        for mode in ("last_block", "all_blocks"):
+            q = qs[qn][(AV_BLOCKS - 1) * qblen:].contiguous() if mode == "last_block" else qs[qn]
+            blocks = [AV_BLOCKS - 1] if mode == "last_block" else list(range(AV_BLOCKS))
+            ids = torch.tensor([seg_of_block[b] for b in blocks for _ in range(qblen)], dtype=torch.int32,
+                               device=dev)
+            out = torch.empty_like(q)
+            us = timed_us(lambda: text.attention(q, 0, 0, None, 0.0, out=out, q_block=ids, same_block=True,
+                                                 stream=stream), stream)
+            pairs = sum(qblen * prompts[seg_of_block[b]] for b in blocks)
+            flop = 4.0 * AV_H * D * pairs
+            nbytes = 2 * AV_H * text.N * D * 2 + 2 * q.shape[0] * AV_H * D * 2
+            res[f"{qn[0]}->t {mode}"] = {
+                "queries": q.shape[0], "slots": text.N, "us": round(us, 2), "gflop": round(flop / 1e9, 3),
+                "tflops": round(flop / (us * 1e-6) / 1e12, 2), "mbytes": round(nbytes / 1e6, 2),
+                "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    # the first block of a take: one latent frame more (1,536 video tokens)
+    first = Ring(1536 + (AV_BLOCKS - 1) * AV_VIDEO, AV_H, D, "bf16", 0.0, device=dev)
+    lens = [1536] + [AV_VIDEO] * (AV_BLOCKS - 1)
+    for b, n in enumerate(lens):
+        first.write(rnd(n), rnd(n), 0, b)
+        if b < AV_BLOCKS - 1:
+            first.advance(n)
+    qf = rnd(first.N)
+    ids = torch.repeat_interleave(torch.arange(AV_BLOCKS, device=dev, dtype=torch.int32),
+                                  torch.tensor(lens, device=dev))
+    out = torch.empty_like(qf)
+    need = first.workspace_bytes(first.N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    us = timed_us(lambda: first.attention(qf, 0, 0, None, 0.0, out=out, workspace=ws, q_block=ids, stream=stream),
+                  stream)
+    csum = [sum(lens[:b + 1]) for b in range(AV_BLOCKS)]
+    flop = 4.0 * AV_H * D * sum(lens[b] * csum[b] for b in range(AV_BLOCKS))
+    res["v->v all_blocks first_block_shape"] = {
+        "queries": first.N, "slots": first.N, "us": round(us, 2), "gflop": round(flop / 1e9, 3),
+        "tflops": round(flop / (us * 1e-6) / 1e12, 2),
+        "frac_bf16_peak": round(flop / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     for qn, kn in (("video", "video"), ("audio", "audio"), ("video", "audio"), ("audio", "video")):
         ring, kblen = rings[kn]
         qblen = rings[qn][1]

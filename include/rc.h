@@ -182,6 +182,33 @@ rc_status rc_chunk_attention(const rc_ring* ring, const void* q, int32_t n_q, in
                              float softmax_scale, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Masks of rc_chunk_attention_ex. */
+typedef enum {
+  RC_MASK_BLOCK_CAUSAL = 0, /* slot_block != -1 and slot_block <= block(i); bias on earlier blocks */
+  RC_MASK_SAME_BLOCK = 1    /* slot_block == block(i) (>= 0); no bias */
+} rc_mask;
+
+/*
+ * rc_chunk_attention with explicit query blocks and a choice of mask, for
+ * the joint audio-video block (StreamLTX project page, Training and Data):
+ *   q_block   device [n_q] int32 block id of every query (>= 0), or NULL for
+ *             q_block0 + i / q_block_len.  Blocks of unequal length occur when
+ *             the first block of a take carries one latent frame more (4 + 3k
+ *             video and 26 + 25k audio frames).
+ *   mask      RC_MASK_BLOCK_CAUSAL as rc_chunk_attention, or RC_MASK_SAME_BLOCK
+ *             for the text cross-attention paths, where each block sees only
+ *             the prompt of its own segment: text slots carry their segment's
+ *             id as block id, queries their block's segment id, and slot s is
+ *             visible to query i iff slot_block[s] == block(i); cache_bias is
+ *             not applied.
+ * Everything else as rc_chunk_attention (which is this call with q_block =
+ * NULL and RC_MASK_BLOCK_CAUSAL).
+ */
+rc_status rc_chunk_attention_ex(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0,
+                                const int32_t* q_block, int32_t q_block0, int32_t q_block_len, int32_t mask,
+                                float cache_bias, float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace that lets rc_chunk_attention use its full key split for n_q queries. */
 size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
 

@@ -23,6 +23,16 @@ For query i: pos_i = q_pos0 + i, b_i = q_block0 + floor(i / q_block_len),
     out_i  = sum_s softmax_s(l_is) v_s,   lse_i = ln sum_s exp(l_is)
 sigma = softmax_scale, or 1/sqrt(d) when 0 is given.  A query with no
 visible slot gets out = 0 and lse = -inf.
+
+Two generalisations serve the joint audio-video block (StreamLTX project
+page, Training and Data):
+* per-query blocks: b_i may be given for every query (the first block of a
+  take carries one latent frame more than the others -- 4 + 3k video and
+  26 + 25k audio frames -- so blocks of queries are not all one length);
+* the same-block mask for the text cross-attention paths: each block sees
+  only the prompt of its own segment.  The text slots carry their segment's
+  id as block id, each query its block's segment id, and slot s is visible
+  to query i iff blk_s == b_i (no bias: the prompt is not history).
 """
 from __future__ import annotations
 
@@ -35,10 +45,18 @@ def query_blocks(n_q: int, q_block0: int, q_block_len: int) -> np.ndarray:
     return q_block0 + np.arange(n_q) // q_block_len
 
 
-def visibility(slot_block: np.ndarray, qblk: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """(visible, earlier_block) boolean masks of shape [n_q][N]."""
+def visibility(slot_block: np.ndarray, qblk: np.ndarray, mask: str = "causal"
+               ) -> tuple[np.ndarray, np.ndarray]:
+    """(visible, earlier_block) boolean masks of shape [n_q][N].
+    mask "causal": visible iff blk != -1 and blk <= b_i, bias on blk < b_i;
+    mask "same": visible iff blk == b_i (>= 0), never biased."""
     blk = np.asarray(slot_block)[None, :]
     qb = np.asarray(qblk)[:, None]
+    if mask == "same":
+        vis = (blk != -1) & (blk == qb)
+        return vis, np.zeros_like(vis)
+    if mask != "causal":
+        raise ValueError(mask)
     vis = (blk != -1) & (blk <= qb)
     earlier = vis & (blk < qb)
     return vis, earlier
@@ -46,8 +64,11 @@ def visibility(slot_block: np.ndarray, qblk: np.ndarray) -> tuple[np.ndarray, np
 
 def chunk_attention(k_vals: np.ndarray, v_vals: np.ndarray, slot_block: np.ndarray,
                     q: np.ndarray, q_pos0: int, q_block0: int, q_block_len: int,
-                    cache_bias: float, softmax_scale: float, rope_base: float):
+                    cache_bias: float, softmax_scale: float, rope_base: float,
+                    q_blocks=None, mask: str = "causal"):
     """k_vals, v_vals: float64 [H][N][d]; q: float64 [n_q][H][d] (unrotated).
+    q_blocks: optional [n_q] block ids (then q_block0 and q_block_len are
+    not used); mask: "causal" or "same".
 
     Returns (out float64 [n_q][H][d], lse float64 [H][n_q])."""
     H, N, d = k_vals.shape
@@ -55,7 +76,9 @@ def chunk_attention(k_vals: np.ndarray, v_vals: np.ndarray, slot_block: np.ndarr
     sigma = softmax_scale if softmax_scale != 0 else 1.0 / np.sqrt(d)
     pos = q_pos0 + np.arange(n_q)
     qr = rope(q, pos[:, None], rope_base)
-    vis, earlier = visibility(slot_block, query_blocks(n_q, q_block0, q_block_len))
+    qblk = (query_blocks(n_q, q_block0, q_block_len) if q_blocks is None
+            else np.asarray(q_blocks, dtype=np.int64))
+    vis, earlier = visibility(slot_block, qblk, mask)
     bias = np.where(earlier, float(cache_bias), 0.0)
     any_vis = vis.any(axis=1)
     out = np.zeros((n_q, H, d), dtype=np.float64)
@@ -73,8 +96,9 @@ def chunk_attention(k_vals: np.ndarray, v_vals: np.ndarray, slot_block: np.ndarr
     return out, lse
 
 
-def ring_attention(ring, q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale=0.0):
+def ring_attention(ring, q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale=0.0,
+                   q_blocks=None, mask="causal"):
     """chunk_attention over an oracle Ring."""
     return chunk_attention(ring.k_values(), ring.v_values(), ring.slot_block, q,
                            q_pos0, q_block0, q_block_len, cache_bias, softmax_scale,
-                           ring.rope_base)
+                           ring.rope_base, q_blocks=q_blocks, mask=mask)

@@ -102,6 +102,16 @@ WORKLOADS = {
     "av": Workload("av", heads=32, head_dim=128, n_slots=11520, n_new=1152,
                    kv_dtype="bf16", rope_base=0.0, seed=3, cache_bias=0.0,
                    extra={"video_block": 1152, "audio_block": 25, "blocks": 10}),
+    # Six-path joint audio-video block (StreamLTX project page, Training and
+    # Data): the first block carries one latent frame more (4 + 3k video
+    # frames of 16 x 24 tokens, 26 + 25k audio frames), and three prompt
+    # segments (blocks 0-3, 4-6, 7-9) feed the text cross-attention; the
+    # prompt lengths are not on the page (96-160 tokens stand in).
+    "av6": Workload("av6", heads=32, head_dim=128, n_slots=1536 + 9 * 1152, n_new=1152,
+                    kv_dtype="bf16", rope_base=0.0, seed=5, cache_bias=0.0,
+                    extra={"video_first": 1536, "video_block": 1152, "audio_first": 26, "audio_block": 25,
+                           "blocks": 10, "segment_of_block": [0, 0, 0, 0, 1, 1, 1, 2, 2, 2],
+                           "prompt_tokens": [128, 96, 160]}),
     # Long run: 2000 chunks with eviction, resets every 300 chunks and
     # 10 bias ramps 0 -> -4 -> 0.
     "longrun": Workload("longrun", heads=40, head_dim=128, n_slots=5788, n_new=757,

@@ -265,3 +265,16 @@ def test_key_mass_checks():
     assert call(scale=-1.0) == RC_ERR_ARG
     assert call(ring=fake_ring(100, kv=RC_BF16)) == RC_ERR_UNSUPPORTED
     assert L.rc_key_mass_workspace_bytes(ctypes.byref(fake_ring(100, kv=RC_BF16)), 70) == 0
+
+
+def test_attention_ex_checks():
+    L = lib()
+    r = fake_ring(100)
+
+    def call(qb=0, bl=10, mask=0):
+        return L.rc_chunk_attention_ex(ctypes.byref(r), FAKE, 10, 0, qb, 0, bl, mask, 0.0, 0.0, FAKE, None, 0, 0,
+                                       None)
+    assert call(mask=2) == RC_ERR_ARG
+    assert call(mask=-1) == RC_ERR_ARG
+    assert call(bl=0) == RC_ERR_ARG            # no block array and no block length
+    assert call(qb=FAKE + 2, bl=0) == RC_ERR_ARG   # misaligned block array

@@ -18,7 +18,7 @@ import torch
 
 from autoregressive_video_diffusion_ring_amd import RcError, Ring
 from oracle import e4m3
-from oracle.attention import ring_attention, visibility, query_blocks
+from oracle.attention import chunk_attention, ring_attention, visibility, query_blocks
 from oracle.ring import Ring as OracleRing
 from synthetic_inputs import WORKLOADS
 
@@ -377,6 +377,66 @@ def test_joint_av_four_paths():
         ref_all, _ = oracle_rows(oring, q, rows_all, 0, 0, blen, 0.0)
         assert_attention_close(out_all, ref_all, "bf16", rows=rows_all)
         print(f"  {name}: ok", flush=True)
+
+
+def test_joint_av_six_paths_first_block():
+    """All six paths of the joint block with the first block one frame
+    longer (1,536 video / 26 audio tokens, then 1,152 / 25) and three prompt
+    segments: the four cache paths with per-query blocks (all ten blocks as
+    queries, block-causal), and video->text, audio->text with the same-block
+    mask (each block sees only its own segment's prompt)."""
+    w = WORKLOADS["av6"]
+    banner("joint A/V six paths: first block 1536/26, 3 prompt segments, bf16 H=32")
+    rng = np.random.default_rng(w.seed)
+    H, d, B = w.heads, w.head_dim, w.extra["blocks"]
+    vlen = [w.extra["video_first"]] + [w.extra["video_block"]] * (B - 1)
+    alen = [w.extra["audio_first"]] + [w.extra["audio_block"]] * (B - 1)
+    seg, plen = w.extra["segment_of_block"], w.extra["prompt_tokens"]
+    gv, ov = make_pair(sum(vlen), H, d, "bf16", 0.0)
+    ga, oa = make_pair(sum(alen), H, d, "bf16", 0.0)
+    gt, ot = make_pair(sum(plen), H, d, "bf16", 0.0)
+    for b in range(B):
+        write_both(gv, ov, rng, vlen[b], sum(vlen[:b]), b)
+        write_both(ga, oa, rng, alen[b], sum(alen[:b]), b)
+        for g_, o_, n_ in ((gv, ov, vlen[b]), (ga, oa, alen[b])):
+            if b < B - 1:
+                g_.advance(n_)
+                o_.advance(n_)
+    for sgm, n in enumerate(plen):   # each prompt's tokens carry their segment id as block id
+        write_both(gt, ot, rng, n, 0, sgm)
+        if sgm < len(plen) - 1:
+            gt.advance(n)
+            ot.advance(n)
+    qv_t, qv = inputs(rng, "bf16", (sum(vlen), H, d))
+    qa_t, qa = inputs(rng, "bf16", (sum(alen), H, d))
+    vblk = np.repeat(np.arange(B), vlen).astype(np.int32)
+    ablk = np.repeat(np.arange(B), alen).astype(np.int32)
+    vseg = np.asarray(seg, dtype=np.int32)[vblk]
+    aseg = np.asarray(seg, dtype=np.int32)[ablk]
+    rings = {"v": (gv, oracle_from_gpu(gv, 0.0)), "a": (ga, oracle_from_gpu(ga, 0.0)),
+             "t": (gt, oracle_from_gpu(gt, 0.0))}
+    queries = {"v": (qv_t, qv, vblk, vseg), "a": (qa_t, qa, ablk, aseg)}
+    for qn, kn in (("v", "v"), ("a", "a"), ("v", "a"), ("a", "v"), ("v", "t"), ("a", "t")):
+        gring, oring = rings[kn]
+        qt, q, qblk, qseg = queries[qn]
+        same = kn == "t"
+        ids = qseg if same else qblk
+        out = gring.attention(qt, 0, 0, None, -0.4, q_block=torch.from_numpy(ids).to(DEV), same_block=same)
+        n = q.shape[0]
+        rows = np.unique(np.r_[0:n:max(1, n // 50), n - 1, 1535 if qn == "v" else 25, 1536 if qn == "v" else 26])
+        rows = rows[rows < n]
+        ref, _ = chunk_attention(oring.k_values(), oring.v_values(), oring.slot_block, q[rows], 0, 0, 1, -0.4, 0.0,
+                                 0.0, q_blocks=ids[rows], mask="same" if same else "causal")
+        assert_attention_close(out, ref, "bf16", rows=rows)
+        print(f"  {qn}->{kn}: ok", flush=True)
+    # streaming: the last block of video against its own segment's prompt
+    last = vblk == B - 1
+    out = gt.attention(qv_t[torch.from_numpy(last).to(DEV)].contiguous(), 0, seg[B - 1], int(last.sum()), 0.0,
+                       same_block=True)
+    sl = ot.slot_block == seg[B - 1]
+    ref, _ = chunk_attention(ot.k_values()[:, sl], ot.v_values()[:, sl], np.zeros(sl.sum(), np.int64), qv[last],
+                             0, 0, int(last.sum()), 0.0, 0.0, 0.0)
+    assert_attention_close(out, ref, "bf16")
 
 
 def test_split_kv_matches_unsplit():

@@ -12,6 +12,11 @@
   nothing; the rows of block b in a multi-block query equal a streaming call
   for block b alone; RoPE on both sides makes a position shift of queries
   and keys invisible.
+* Per-query blocks and the same-block mask: an explicit block array equal
+  to the (q_block0, q_block_len) formula gives the same result; blocks of
+  unequal length (the first block one frame longer) follow the brute-force
+  loop; the same-block mask equals, block by block, plain attention over
+  only that block's slots (a different route: slicing, no mask).
 """
 import math
 
@@ -212,3 +217,48 @@ def test_two_key_closed_form():
         w0 = math.exp(1.0 + b) / (math.exp(1.0 + b) + 1.0)
         assert np.allclose(out[0, 0], [2 * w0, 3 * (1 - w0)], atol=1e-15)
         assert abs(lse[0, 0] - math.log(math.exp(1 + b) + 1)) < 1e-15
+
+
+def test_query_block_array_equals_formula():
+    ring, q, w = tiny_ring_and_queries()
+    a = ring_attention(ring, q, 96, 2, 10, -0.5)
+    qb = 2 + np.arange(q.shape[0]) // 10
+    b = ring_attention(ring, q, 96, 0, 1, -0.5, q_blocks=qb)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_unequal_blocks_brute_force():
+    """Queries in blocks of 12, 10 and 10 (a longer first block): each query
+    row equals the brute-force loop run for that query alone."""
+    ring, q, w = tiny_ring_and_queries()
+    sizes = [12, 10, 10]
+    qb = np.repeat([1, 2, 3], sizes)
+    out, lse = ring_attention(ring, q, 96, 0, 1, -0.5, q_blocks=qb)
+    sigma = 1 / math.sqrt(q.shape[2])
+    for i in (0, 11, 12, 21, 22, 31):
+        ref, ref_lse = brute_force(ring, q[i:i + 1], 96 + i, int(qb[i]), 1, -0.5, sigma)
+        assert np.max(np.abs(out[i] - ref[0])) < 1e-12
+        assert np.max(np.abs(lse[:, i] - ref_lse[:, 0])) < 1e-12
+
+
+def test_same_block_mask_equals_sliced_plain_attention():
+    """Text cross-attention: 3 segments' prompts (block ids 0, 1, 2; one slot
+    empty), queries of segments 2, 0, 1.  Each query block's rows equal plain
+    attention over only that segment's slots, with every slot relabelled
+    into one visible block."""
+    rng = np.random.default_rng(9)
+    H, d, N = 2, 16, 40
+    blk = np.array([0] * 12 + [1] * 9 + [2] * 18 + [-1])
+    k = rng.standard_normal((H, N, d))
+    v = rng.standard_normal((H, N, d))
+    q = rng.standard_normal((15, H, d))
+    qb = np.repeat([2, 0, 1], 5)
+    out, lse = chunk_attention(k, v, blk, q, 0, 0, 1, -3.0, 0.0, 0.0, q_blocks=qb, mask="same")
+    for seg in (0, 1, 2):
+        rows, cols = qb == seg, blk == seg
+        ref, ref_lse = chunk_attention(k[:, cols], v[:, cols], np.zeros(cols.sum(), np.int64), q[rows],
+                                       0, 0, rows.sum(), -3.0, 0.0, 0.0)
+        assert np.allclose(out[rows], ref, atol=1e-13) and np.allclose(lse[:, rows], ref_lse, atol=1e-13)
+    # a segment with no text slots: zero output, lse -inf
+    out2, lse2 = chunk_attention(k, v, blk, q[:3], 0, 0, 1, 0.0, 0.0, 0.0, q_blocks=[3, 3, 3], mask="same")
+    assert np.all(out2 == 0) and np.all(lse2 == -np.inf)
