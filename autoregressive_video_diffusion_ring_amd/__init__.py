@@ -26,6 +26,7 @@ __all__ = [
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
     "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_workspace_bytes", "rc_cache_write_scored",
     "rc_cache_write_scored_workspace_bytes", "rc_chunk_attention_ex", "RC_MASK_BLOCK_CAUSAL", "RC_MASK_SAME_BLOCK",
+    "rc_qkv_project_write", "rc_qkv_workspace_bytes",
 ]
 
 
@@ -96,6 +97,16 @@ def rc_chunk_attention_ex(ring: RcRing, q, n_q: int, q_pos0: int, q_block, q_blo
     check(lib().rc_chunk_attention_ex(ctypes.byref(ring), _ptr(q), n_q, q_pos0, _ptr(q_block), q_block0,
                                       q_block_len, mask, float(cache_bias), float(softmax_scale), _ptr(out),
                                       _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rc_qkv_project_write(ring: RcRing, x, n: int, C: int, w, w_scale, pos0: int, block_id: int, q_out, workspace,
+                         workspace_bytes: int, stream=None) -> None:
+    check(lib().rc_qkv_project_write(ctypes.byref(ring), _ptr(x), n, C, _ptr(w), _ptr(w_scale), pos0, block_id,
+                                     _ptr(q_out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def rc_qkv_workspace_bytes(n: int, C: int) -> int:
+    return lib().rc_qkv_workspace_bytes(n, C)
 
 
 def rc_attention_workspace_bytes(ring: RcRing, n_q: int) -> int:
@@ -209,6 +220,23 @@ class Ring:
         rc_key_mass(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias, softmax_scale, lse,
                     mass, workspace, ws_bytes, stream)
         return mass
+
+    def project_write(self, x, w, w_scale, pos0: int, block_id: int, q_out=None, workspace=None, stream=None):
+        """Fused QKV projection + cache write of the tokens of x [n][C] (bf16);
+        w: uint8 e4m3 codes [3 H d][C], w_scale float32 [3 H d].  Returns q
+        [n][H][d] (bf16, not rotated)."""
+        n, C = x.shape
+        _check_tensor(x, "x", torch.bfloat16, (n, C), self.device)
+        _check_tensor(w, "w", torch.uint8, (3 * self.H * self.d, C), self.device)
+        _check_tensor(w_scale, "w_scale", torch.float32, (3 * self.H * self.d,), self.device)
+        if q_out is None:
+            q_out = torch.empty((n, self.H, self.d), dtype=torch.bfloat16, device=self.device)
+        _check_tensor(q_out, "q_out", torch.bfloat16, (n, self.H, self.d), self.device)
+        if workspace is None:
+            workspace = torch.empty(max(rc_qkv_workspace_bytes(n, C), 16), dtype=torch.uint8, device=self.device)
+        rc_qkv_project_write(self.struct, x, n, C, w, w_scale, pos0, block_id, q_out, workspace,
+                             workspace.numel() * workspace.element_size(), stream)
+        return q_out
 
     def rerotate(self, delta: int, stream=None) -> None:
         rc_cache_rerotate(self.struct, delta, stream)

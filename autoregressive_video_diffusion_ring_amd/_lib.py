@@ -51,6 +51,9 @@ SIGNATURES = {
     "rc_chunk_attention_ex": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
                                         c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "rc_attention_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
+    "rc_qkv_project_write": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32,
+                                       c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "rc_qkv_workspace_bytes": (c_size_t, [c_int32, c_int32]),
     "rc_ring_advance": (c_int32, [POINTER(RcRing), c_int32]),
     "rc_key_mass": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,
                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -110,35 +110,6 @@ __device__ __forceinline__ void unpack(const Raw<KV, EPL>& r, float* x) {
   }
 }
 
-// x / scale rounded to float32 with round-to-odd, so that the FP8 conversion
-// that follows (round to nearest even) yields the correctly rounded code of
-// the exact quotient.  A plain float32 quotient can land exactly on a
-// midpoint between two FP8 codes when the exact quotient lies just beside it
-// (common for unrotated input: x and the absmax carry 8 significant bits, so
-// 448 x / absmax is often a short fraction, while scale = absmax / 448 is
-// rounded), and the conversion's tie-break would then round the wrong way.
-// Round-to-odd keeps the "inexact" information in the last bit (float32 has
-// 20 more bits than e4m3), the classical remedy for double rounding.
-//
-// The quotient comes from rcp ~ 1/scale and one Newton step, which leaves it
-// within one ulp of x / scale; the remainder x - q scale is then exact (one
-// FMA), and its sign gives the truncation and the sticky bit.  Callers pass
-// rcp = 0 for an all-zero row (scale 0), which yields 0.
-__device__ __forceinline__ float qdiv_rto(float x, float scale, float rcp) {
-  const float q0 = x * rcp;
-  const float e0 = fmaf(-q0, scale, x);
-  const float q = fmaf(e0, rcp, q0);
-  const float e = fmaf(-q, scale, x);
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t t = (u - ((__float_as_uint(e) ^ u) >> 31)) | 1u;  // toward zero if e opposes q
-  return e == 0.f ? q : __uint_as_float(t);
-}
-
-// Reciprocal of a row scale for the quotients above (0 for a zero row).
-__device__ __forceinline__ float scale_rcp(float scale) {
-  return scale > 0.f ? __builtin_amdgcn_rcpf(scale) : 0.f;
-}
-
 // Encodes EPL values as FP8 codes of the given scale.  EXACT: correctly
 // rounded codes of the exact quotients (needed where inputs are short
 // binary fractions, so that ties are common); otherwise the float32 product

@@ -249,6 +249,37 @@ rc_status rc_cache_write_scored(rc_ring* r, const void* k_new, const void* v_new
   return st;
 }
 
+size_t rc_qkv_workspace_bytes(int32_t n, int32_t C) {
+  if (n < 1 || C < 128 || C % 128) return 0;
+  return rc::qkv_workspace_bytes(n, C);
+}
+
+rc_status rc_qkv_project_write(rc_ring* r, const void* x, int32_t n, int32_t C, const uint8_t* w,
+                               const float* w_scale, int32_t pos0, int32_t block_id, void* q_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  rc_status st = check_write(r, x, x, n, pos0, block_id);
+  if (st != RC_OK) return st;
+  if (r->kv_dtype != RC_FP8_E4M3 || r->head_dim != 128)
+    return fail(RC_ERR_UNSUPPORTED, "the fused projection is built for FP8 rings with head_dim 128");
+  if (C < 128 || C % 128 || C > (1 << 16)) return fail(RC_ERR_ARG, "C must be a multiple of 128 in 128..65536 (got %d)", C);
+  if (!w || !w_scale || !q_out) return fail(RC_ERR_ARG, "w / w_scale / q_out is NULL");
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(q_out)) & 15u)
+    return fail(RC_ERR_ARG, "w and q_out must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(w_scale) & 3u) return fail(RC_ERR_ARG, "w_scale must be 4-byte aligned");
+  const size_t need = rc::qkv_workspace_bytes(n, C);
+  if (!workspace || workspace_bytes < need)
+    return fail(RC_ERR_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(RC_ERR_ARG, "workspace must be 16-byte aligned");
+  hipError_t e = rc::launch_qkv_project_write(view(r), x, n, C, w, w_scale, r->head, pos0, block_id, q_out, workspace,
+                                              as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "qkv projection write");
+  if (r->n_cur == 0) r->n_hist = std::min(r->n_hist, ring_end(r) - n);
+  r->n_cur = n;
+  r->cur_pos0 = pos0;
+  r->cur_block = block_id;
+  return ok();
+}
+
 rc_status rc_cache_rerotate(rc_ring* r, int32_t delta, void* stream) {
   rc_status st = check_ring(r);
   if (st != RC_OK) return st;

@@ -66,6 +66,12 @@ size_t memory_workspace_bytes(int n_memory, int n_new);
 hipError_t launch_memory_update(const RingView& r, const float* key_score, float gamma, int head, int n_new,
                                 int n_candidates, void* workspace, hipStream_t s);
 
+// Fused QKV projection (FP8) and cache write (qkv_write.hip); d = 128.
+size_t qkv_workspace_bytes(int n, int C);
+hipError_t launch_qkv_project_write(const RingView& r, const void* x, int n, int C, const uint8_t* w,
+                                    const float* w_scale, int head, int pos0, int block_id, void* q_out,
+                                    void* workspace, hipStream_t s);
+
 hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
                                    uint8_t* mask, hipStream_t s);
 

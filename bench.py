@@ -24,7 +24,9 @@ one-second blocks of 1,152 video and 25 audio tokens, 10 blocks cached, 32
 heads, bf16, block-causal; Data: each block sees only its own segment's
 prompt, here three prompts of 96-160 tokens), each with the last block's
 queries and with all ten blocks' queries, and video self-attention with the
-first block one latent frame longer (1,536 tokens).
+first block one latent frame longer (1,536 tokens).  ``qkv_projection`` times
+the fused QKV projection + cache write (FP8 GEMM 757 x 5120 x 15360 with the
+write in its epilogue) beside the unfused bf16 library GEMM + rc_cache_write.
 
 ``--longrun K`` instead runs K chunks of the long-run schedule (a position
 reset every 300 chunks by a delta rotation of all 60 rings, ten cache-bias
@@ -220,6 +222,47 @@ def joint_av(dev, stream) -> dict:
                 "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                 "mbytes": round(nbytes / 1e6, 2), "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     return res
+
+
+def qkv_projection(dev, stream) -> dict:
+    """The fused QKV projection + cache write of one streaming layer call
+    (757 tokens, width C = H d = 5,120, FP8 operands, 40 heads of 128):
+    2 * 757 * 5120 * 15360 = 119.1 GFLOP per call.  Beside it, the unfused
+    path a caller would otherwise run: a library bf16 GEMM (torch.matmul,
+    hipBLASLt) producing q, k, v, then rc_cache_write of k and v."""
+    import torch
+
+    from autoregressive_video_diffusion_ring_amd import Ring, rc_qkv_workspace_bytes
+    C = H * D
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    ring = Ring(N, H, D, "fp8", 10000.0, device=dev)
+    hist = torch.randn((HIST, H, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ring.write(hist, hist, 0, 0)
+    ring.advance(HIST)
+    x = torch.randn((NEW, C), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    mag = torch.randint(0, 0x7F, (3 * C, C), generator=gen, device=dev, dtype=torch.int32)
+    sign = torch.randint(0, 2, (3 * C, C), generator=gen, device=dev, dtype=torch.int32) << 7
+    w = (mag | sign).to(torch.uint8)
+    w_scale = torch.full((3 * C,), 1.0 / (64.0 * C ** 0.5), dtype=torch.float32, device=dev)
+    q = torch.empty((NEW, H, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rc_qkv_workspace_bytes(NEW, C), dtype=torch.uint8, device=dev)
+    us = timed_us(lambda: ring.project_write(x, w, w_scale, HIST, 1, q_out=q, workspace=ws, stream=stream), stream)
+    flop = 2.0 * NEW * C * 3 * C
+    wb = torch.randn((3 * C, C), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty((NEW, 3 * C), dtype=torch.bfloat16, device=dev)
+
+    def unfused():
+        torch.matmul(x, wb.t(), out=out)
+        k = out[:, C:2 * C].view(NEW, H, D)
+        v = out[:, 2 * C:].view(NEW, H, D)
+        ring.write(k.contiguous(), v.contiguous(), HIST, 1, stream=stream)
+    us_gemm = timed_us(lambda: torch.matmul(x, wb.t(), out=out), stream)
+    us_unfused = timed_us(unfused, stream)
+    tf = flop / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "gflop": round(flop / 1e9, 2), "tflops": round(tf, 1),
+            "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "unfused_bf16_gemm_us": round(us_gemm, 2), "unfused_gemm_plus_write_us": round(us_unfused, 2)}
 
 
 def chunk_pos0(t: int) -> int:
@@ -510,10 +553,14 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(REROT_BYTES / (rot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
         "joint_av": None,
+        "qkv_projection": None,
     }
     if not args.no_joint_av:
         log("[bench] joint audio-video paths")
         result["joint_av"] = joint_av(dev, stream)
+    if not args.no_joint_av:
+        log("[bench] fused QKV projection + cache write")
+        result["qkv_projection"] = qkv_projection(dev, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (one layer call)")
         result["cpu_baseline"] = cpu_baseline()

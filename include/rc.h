@@ -281,6 +281,34 @@ rc_status rc_cache_write_scored(rc_ring* ring, const void* k_new, const void* v_
 size_t rc_cache_write_scored_workspace_bytes(const rc_ring* ring, int32_t n_new);
 
 /*
+ * The QKV projection with the cache write fused into its epilogue (Runway
+ * Characters, abstract: FP8 GEMMs; RoPE and FP8 quantisation once per write).
+ * For the n tokens of x:
+ *   [q | k | v] = x W^T with FP8 operands: x is quantised per token with the
+ *   cache's rule (scale = max|x_t| / 448, float32; codes round to nearest
+ *   even), W is given as e4m3 codes with one float32 scale per row, and the
+ *   products accumulate in float32.
+ *   x        device [n][C] bfloat16 (the layer input); C a multiple of 128
+ *   w        device [3 H d][C] e4m3 codes: rows 0 .. H d - 1 give q (head-
+ *            major), then k, then v
+ *   w_scale  device [3 H d] float32
+ *   q_out    device [n][H][d] bfloat16: q, not rotated (rc_chunk_attention's
+ *            q input)
+ *   workspace  device scratch of rc_qkv_workspace_bytes(n, C) bytes
+ * k and v are stored into the ring as rc_cache_write would store them (k
+ * rotated at position pos0 + i, both quantised per (token, head), slot
+ * metadata), from their float32 values: they never exist in HBM in another
+ * form.  Same slots, state rules and errors as rc_cache_write.  FP8 rings with
+ * head_dim 128 only (RC_ERR_UNSUPPORTED otherwise).
+ */
+rc_status rc_qkv_project_write(rc_ring* ring, const void* x, int32_t n, int32_t C, const uint8_t* w,
+                               const float* w_scale, int32_t pos0, int32_t block_id, void* q_out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace rc_qkv_project_write needs for n tokens of width C. */
+size_t rc_qkv_workspace_bytes(int32_t n, int32_t C);
+
+/*
  * The visibility predicate used inside rc_chunk_attention, exported for
  * checking: mask[i][s] (device uint8 [n_q][N]) = 0 if slot s is invisible to
  * query i, 1 if visible without the bias (same block), 2 if visible with the

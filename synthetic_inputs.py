@@ -22,6 +22,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
+    "e4m3_codes",
     "bf16_bits_from_f32",
     "bf16_bits_to_f64",
     "normal_bf16",
@@ -49,6 +50,14 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact float64 values of bfloat16 bit patterns."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return u.view(np.float32).astype(np.float64)
+
+
+def e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniformly random finite OCP e4m3fn bytes (magnitude codes 0..0x7E,
+    random sign): synthetic FP8 weights, given to both sides as codes."""
+    mag = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    return mag | sign
 
 
 def normal_bf16(rng: np.random.Generator, shape) -> tuple[np.ndarray, np.ndarray]:
