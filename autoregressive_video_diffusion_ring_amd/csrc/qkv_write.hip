@@ -6,16 +6,21 @@
 // the FP8 matrix cores and its epilogue does the cache write directly: k and
 // v never exist in HBM in any other form than their cached FP8 codes.
 //
-//  * xquant_kernel: one workgroup per token quantises x (bf16) to FP8 with
-//    scale = max|x| / 448 and correctly rounded codes (the cache's rule).
-//  * qkv_proj_kernel: a workgroup computes 256 tokens x 128 output columns
-//    (one head of q, k or v) with 8 waves, two per SIMD; wave w owns tokens
-//    32w .. 32w+31 and all 128 columns (4 MFMA blocks), so every
-//    (token, head) row of the result lies in one wave.  k steps of 128
-//    bytes: the x tile (256 rows) and the W tile (128 rows) of a step move by
-//    direct-to-LDS loads (no registers) into three stages, two steps ahead
-//    of use, rows swizzled in 16-byte chunks so that the 32 rows a wave reads
-//    together spread over the banks.
+//  * xquant_kernel: one workgroup per token quantises x (bf16) to
+//    FP8 with scale = max|x| / 448 and correctly rounded codes (the cache's
+//    rule), stored in 64-byte k slices ([C / 64][token][64]).
+//  * qkv_proj_kernel: a workgroup computes 384 tokens x 128 output columns
+//    (one head of q, k or v) with 12 waves, three per SIMD; wave w owns
+//    tokens 32w .. 32w+31 and all 128 columns (4 MFMA blocks), so every
+//    (token, head) row of the result lies in one wave.  At the streaming
+//    shape (757 tokens, 3 x 40 heads) that is 240 workgroups: one round on
+//    256 CUs.  k steps of 64 bytes: the x tile (384 rows) and the W tile
+//    (128 rows) of a step move by direct-to-LDS loads (no registers) into
+//    four stages, three steps ahead of use, rows swizzled in 16-byte chunks
+//    so that the 32 rows a wave reads together spread over the banks.  The
+//    x slice of a step is contiguous in the workspace, so its loads fetch
+//    whole 128-byte lines (the L2 request rate, not its bandwidth, is what
+//    these loads run into).
 //  * the products are formed as W x^T, so that a lane owns one token: lane
 //    (n, g) of a wave holds, for its token, 64 of the head's 128 output
 //    columns in runs of 4 (the other 64 sit in lane n + 32).

@@ -295,6 +295,8 @@ size_t rc_cache_write_scored_workspace_bytes(const rc_ring* ring, int32_t n_new)
  *   q_out    device [n][H][d] bfloat16: q, not rotated (rc_chunk_attention's
  *            q input)
  *   workspace  device scratch of rc_qkv_workspace_bytes(n, C) bytes
+ * x, w, q_out and workspace must be 16-byte aligned, w_scale 4-byte aligned
+ * (RC_ERR_ARG otherwise).
  * k and v are stored into the ring as rc_cache_write would store them (k
  * rotated at position pos0 + i, both quantised per (token, head), slot
  * metadata), from their float32 values: they never exist in HBM in another

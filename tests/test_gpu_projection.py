@@ -103,6 +103,9 @@ def summation_bounds(x, wc, ws, H, d, order, written):
 
 @pytest.mark.parametrize("n,C,H,N,head0,hist", [
     (100, 256, 2, 300, 250, 0),        # ragged token tile, a write that wraps
+    (1, 128, 1, 64, 10, 0),            # one token, the narrowest input (two k steps)
+    (385, 1024, 3, 1200, 1000, 200),   # a second token tile holding one token; wrap after history
+    (40, 8320, 2, 200, 0, 0),          # input rows wider than one wave holds (two-pass quantiser)
     (757, 5120, 40, 5788, 0, 5031),    # the streaming shape: 757 new tokens after 5,031 of history
 ])
 def test_qkv_project_write(n, C, H, N, head0, hist):
