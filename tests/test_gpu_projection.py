@@ -101,19 +101,22 @@ def summation_bounds(x, wc, ws, H, d, order, written):
     return out
 
 
-@pytest.mark.parametrize("n,C,H,N,head0,hist", [
-    (100, 256, 2, 300, 250, 0),        # ragged token tile, a write that wraps
-    (1, 128, 1, 64, 10, 0),            # one token, the narrowest input (two k steps)
-    (385, 1024, 3, 1200, 1000, 200),   # a second token tile holding one token; wrap after history
-    (40, 8320, 2, 200, 0, 0),          # input rows wider than one wave holds (two-pass quantiser)
-    (757, 5120, 40, 5788, 0, 5031),    # the streaming shape: 757 new tokens after 5,031 of history
+@pytest.mark.parametrize("n,C,H,N,head0,hist,anchor,memory", [
+    (100, 256, 2, 300, 250, 0, 0, 0),         # ragged token tile, a write that wraps
+    (1, 128, 1, 64, 10, 0, 0, 0),             # one token, the narrowest input (two k steps)
+    (385, 1024, 3, 1200, 1000, 200, 0, 0),    # a second token tile holding one token; wrap after history
+    (40, 8320, 2, 200, 0, 0, 0, 0),           # input rows wider than one wave holds (two-pass quantiser)
+    (200, 256, 2, 600, 0, 400, 50, 100),      # anchored ring with a content memory: the write wraps
+                                              # from the memory's first slot (500) to slot 50
+    (757, 5120, 40, 5788, 0, 5031, 0, 0),     # the streaming shape: 757 new tokens after 5,031 of history
 ])
-def test_qkv_project_write(n, C, H, N, head0, hist):
-    banner(f"qkv projection + write: n={n} C={C} H={H} N={N} head0={head0} history {hist}")
+def test_qkv_project_write(n, C, H, N, head0, hist, anchor, memory):
+    banner(f"qkv projection + write: n={n} C={C} H={H} N={N} head0={head0} history {hist} "
+           f"anchor {anchor} memory {memory}")
     rng = np.random.default_rng(71)
     d = 128
-    g = Ring(N, H, d, "fp8", 10000.0, first_slot=head0, device=DEV)
-    o = OracleRing(N, H, d, "fp8", 10000.0, first_slot=head0)
+    g = Ring(N, H, d, "fp8", 10000.0, first_slot=head0, n_anchor=anchor, n_memory=memory, device=DEV)
+    o = OracleRing(N, H, d, "fp8", 10000.0, first_slot=head0, n_anchor=anchor, n_memory=memory)
     if hist:
         kb, k = normal_bf16(rng, (hist, H, d))
         vb, v = normal_bf16(rng, (hist, H, d))
