@@ -6,8 +6,9 @@ kernels behind the C ABI.  The entry points keep the C names:
 
     rc_ring_init, rc_cache_write, rc_cache_rerotate, rc_chunk_attention,
     rc_ring_advance, rc_attention_workspace_bytes, rc_debug_visibility,
-    rc_key_mass, rc_key_mass_workspace_bytes, rc_cache_write_scored,
-    rc_cache_write_scored_workspace_bytes
+    rc_key_mass, rc_key_mass_slots, rc_key_mass_workspace_bytes,
+    rc_cache_write_scored, rc_cache_write_scored_workspace_bytes,
+    rc_chunk_attention_ex, rc_qkv_project_write, rc_qkv_workspace_bytes
 
 and ``Ring`` owns a ring's device buffers (torch tensors) and its rc_ring
 struct.  See include/rc.h for the meaning of every argument.
@@ -24,7 +25,8 @@ from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, R
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
-    "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_workspace_bytes", "rc_cache_write_scored",
+    "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_slots", "rc_key_mass_workspace_bytes",
+    "rc_cache_write_scored",
     "rc_cache_write_scored_workspace_bytes", "rc_chunk_attention_ex", "RC_MASK_BLOCK_CAUSAL", "RC_MASK_SAME_BLOCK",
     "rc_qkv_project_write", "rc_qkv_workspace_bytes",
 ]
@@ -124,6 +126,16 @@ def rc_key_mass(ring: RcRing, q, n_q: int, q_pos0: int, q_block0: int, q_block_l
                             _stream(stream)))
 
 
+def rc_key_mass_slots(ring: RcRing, q, n_q: int, q_pos0: int, q_block0: int, q_block_len: int, cache_bias: float,
+                      softmax_scale: float, lse, ranges, mass, workspace, workspace_bytes: int, stream=None) -> None:
+    """ranges: a sequence of (lo, hi) slot ranges (host ints)."""
+    flat = [int(v) for pair in ranges for v in pair]
+    arr = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+    check(lib().rc_key_mass_slots(ctypes.byref(ring), _ptr(q), n_q, q_pos0, q_block0, q_block_len,
+                                  float(cache_bias), float(softmax_scale), _ptr(lse), arr, len(flat) // 2,
+                                  _ptr(mass), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def rc_key_mass_workspace_bytes(ring: RcRing, n_q: int) -> int:
     return lib().rc_key_mass_workspace_bytes(ctypes.byref(ring), n_q)
 
@@ -204,9 +216,10 @@ class Ring:
                               ws_bytes, stream)
 
     def key_mass(self, q, q_pos0: int, q_block0: int, q_block_len: int | None, cache_bias: float, lse,
-                 mass=None, softmax_scale: float = 0.0, workspace=None, stream=None):
+                 mass=None, softmax_scale: float = 0.0, workspace=None, stream=None, ranges=None):
         """Accumulate the attention mass of q's rows into mass [H][v_ld]
-        (a new zero tensor when None); lse is rc_chunk_attention's output."""
+        (a new zero tensor when None); lse is rc_chunk_attention's output.
+        ranges: optional (lo, hi) slot ranges; only their slots are scored."""
         n_q = q.shape[0]
         _check_tensor(q, "q", self.input_dtype, (n_q, self.H, self.d), self.device)
         _check_tensor(lse, "lse", torch.float32, (self.H, n_q), self.device)
@@ -217,8 +230,12 @@ class Ring:
             need = rc_key_mass_workspace_bytes(self.struct, n_q)
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
         ws_bytes = workspace.numel() * workspace.element_size()
-        rc_key_mass(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias, softmax_scale, lse,
-                    mass, workspace, ws_bytes, stream)
+        if ranges is None:
+            rc_key_mass(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias, softmax_scale, lse,
+                        mass, workspace, ws_bytes, stream)
+        else:
+            rc_key_mass_slots(self.struct, q, n_q, q_pos0, q_block0, q_block_len or n_q, cache_bias, softmax_scale,
+                              lse, ranges, mass, workspace, ws_bytes, stream)
         return mass
 
     def project_write(self, x, w, w_scale, pos0: int, block_id: int, q_out=None, workspace=None, stream=None):

@@ -57,6 +57,9 @@ SIGNATURES = {
     "rc_ring_advance": (c_int32, [POINTER(RcRing), c_int32]),
     "rc_key_mass": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,
                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "rc_key_mass_slots": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
+                                    c_float, c_void_p, POINTER(c_int32), c_int32, c_void_p, c_void_p, c_size_t,
+                                    c_void_p]),
     "rc_key_mass_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
     "rc_cache_write_scored": (c_int32, [POINTER(RcRing), c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                         c_float, c_void_p, c_size_t, c_void_p]),

@@ -51,6 +51,7 @@ constexpr int kMassWaves = 16;     // waves (x 32 slots) per mass workgroup
 constexpr int kMassThreads = kMassWaves * kWave;
 constexpr int kMassSlots = kMassWaves * 32;
 constexpr int kChunkTiles = 8;     // prepared tiles per LDS buffer
+constexpr int kMassListGroups = 64;  // slot groups a restricted call lists (else it runs all)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -84,6 +85,12 @@ struct MassArgs {
   float bias_log2, scale_log2;
   int use_rope;
   RopeTable rope;
+  // optional restriction to slot ranges [lo, hi): only the slot groups that
+  // meet a range run (n_groups of them, listed), and only slots inside a
+  // range receive mass
+  int n_ranges, range_lo[kMassRanges], range_hi[kMassRanges];
+  int n_groups;
+  int16_t group_id[kMassListGroups];
 };
 
 template <int D>
@@ -163,9 +170,10 @@ __global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
   const int n = lane & 31, g = lane >> 5;
   int item = blockIdx.x;
   if (a.remap) item = (item % 8) * (a.items / 8) + item / 8;  // one head's groups on one XCD
-  const int groups = a.v_ld / kMassSlots + (a.v_ld % kMassSlots != 0);
+  const int groups = a.n_groups > 0 ? a.n_groups : a.v_ld / kMassSlots + (a.v_ld % kMassSlots != 0);
   const int h = item / groups;
-  const int slot0 = (item % groups) * kMassSlots + 32 * wave;
+  const int grp = a.n_groups > 0 ? a.group_id[item % groups] : item % groups;
+  const int slot0 = grp * kMassSlots + 32 * wave;
   const bool active = slot0 < a.v_ld;  // v_ld is a multiple of 64: a wave's slots are all real or all absent
   const int slot = active ? slot0 + n : 0;
 
@@ -271,7 +279,11 @@ __global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
   // lanes n and n + 32 hold the same slot (different queries)
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
   const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  if (active && g == 0) {
+  bool wanted = a.n_ranges == 0;
+#pragma unroll
+  for (int i = 0; i < kMassRanges; ++i)
+    wanted = wanted || (i < a.n_ranges && slot >= a.range_lo[i] && slot < a.range_hi[i]);
+  if (active && g == 0 && wanted) {
     float* m = a.mass + static_cast<size_t>(h) * a.v_ld + slot;
     *m += total;
   }
@@ -531,7 +543,8 @@ __global__ __launch_bounds__(256) void memory_move_kernel(RingView r, SelArgs a)
 }
 
 template <int D>
-hipError_t mass_impl(const RingView& r, const AttnCall& c, const float* lse, float* mass, hipStream_t s) {
+hipError_t mass_impl(const RingView& r, const AttnCall& c, const float* lse, float* mass, const int* ranges,
+                     int n_ranges, hipStream_t s) {
   MassArgs a{};
   a.k = static_cast<const uint8_t*>(r.k);
   a.k_scale = r.k_scale;
@@ -557,7 +570,27 @@ hipError_t mass_impl(const RingView& r, const AttnCall& c, const float* lse, flo
   hipLaunchKernelGGL((mass_prep_kernel<D>), dim3((preps + 3) / 4), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int groups = (r.v_ld + kMassSlots - 1) / kMassSlots;
+  int groups = (r.v_ld + kMassSlots - 1) / kMassSlots;
+  a.n_ranges = n_ranges;
+  if (n_ranges > 0) {
+    for (int i = 0; i < n_ranges; ++i) {
+      a.range_lo[i] = ranges[2 * i];
+      a.range_hi[i] = ranges[2 * i + 1];
+    }
+    int listed = 0;
+    for (int gi = 0; gi < groups; ++gi) {
+      bool meets = false;
+      for (int i = 0; i < n_ranges; ++i)
+        meets = meets || (a.range_lo[i] < (gi + 1) * kMassSlots && a.range_hi[i] > gi * kMassSlots);
+      if (meets && listed < kMassListGroups) a.group_id[listed] = static_cast<int16_t>(gi);
+      listed += meets ? 1 : 0;
+    }
+    if (listed == 0) return hipSuccess;  // nothing to compute
+    if (listed <= kMassListGroups) {
+      a.n_groups = listed;
+      groups = listed;
+    }  // else: every group runs; the range test still limits what is written
+  }
   a.items = r.H * groups;
   a.remap = a.items % 8 == 0 ? 1 : 0;
   hipLaunchKernelGGL((key_mass_kernel<D>), dim3(a.items), dim3(kMassThreads), 0, s, a);
@@ -574,9 +607,10 @@ size_t key_mass_workspace_bytes(const RingView& r, int n_q) {
   return static_cast<size_t>(r.H) * ((n_q + kMQ - 1) / kMQ) * rec;
 }
 
-hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* lse, float* mass, hipStream_t s) {
-  if (r.kv == KV_FP8 && r.d == 128) return mass_impl<128>(r, c, lse, mass, s);
-  if (r.kv == KV_FP8 && r.d == 64) return mass_impl<64>(r, c, lse, mass, s);
+hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* lse, float* mass, const int* ranges,
+                           int n_ranges, hipStream_t s) {
+  if (r.kv == KV_FP8 && r.d == 128) return mass_impl<128>(r, c, lse, mass, ranges, n_ranges, s);
+  if (r.kv == KV_FP8 && r.d == 64) return mass_impl<64>(r, c, lse, mass, ranges, n_ranges, s);
   return hipErrorInvalidValue;
 }
 

@@ -341,9 +341,11 @@ size_t rc_key_mass_workspace_bytes(const rc_ring* r, int32_t n_q) {
   return rc::key_mass_workspace_bytes(view(r), n_q);
 }
 
-rc_status rc_key_mass(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
-                      int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse, float* mass,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+rc_status key_mass_impl(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                        int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse,
+                        const int32_t* ranges, int32_t n_ranges, float* mass, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   rc_status st = check_ring(r);
   if (st != RC_OK) return st;
   if (!rc::key_mass_supported(r->kv_dtype, r->head_dim))
@@ -363,11 +365,35 @@ rc_status rc_key_mass(const rc_ring* r, const void* q, int32_t n_q, int32_t q_po
   if (!workspace || workspace_bytes < need)
     return fail(RC_ERR_ARG, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(RC_ERR_ARG, "workspace must be 16-byte aligned");
+  if (n_ranges < 0 || n_ranges > rc::kMassRanges)
+    return fail(RC_ERR_ARG, "n_ranges must be in 0..%d (got %d)", rc::kMassRanges, n_ranges);
+  if (n_ranges > 0 && !ranges) return fail(RC_ERR_ARG, "ranges is NULL");
+  for (int i = 0; i < n_ranges; ++i)
+    if (ranges[2 * i] < 0 || ranges[2 * i] >= ranges[2 * i + 1] || ranges[2 * i + 1] > r->n_slots)
+      return fail(RC_ERR_ARG, "range %d [%d, %d) must satisfy 0 <= lo < hi <= n_slots (%d)", i, ranges[2 * i],
+                  ranges[2 * i + 1], r->n_slots);
   rc::AttnCall c{q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, nullptr, nullptr, workspace,
                  workspace_bytes};
-  hipError_t e = rc::launch_key_mass(view(r), c, lse, mass, as_stream(stream));
+  hipError_t e = rc::launch_key_mass(view(r), c, lse, mass, ranges, n_ranges, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "key mass");
   return ok();
+}
+}  // namespace
+
+rc_status rc_key_mass(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                      int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse, float* mass,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return key_mass_impl(r, q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, lse, nullptr, 0, mass,
+                       workspace, workspace_bytes, stream);
+}
+
+rc_status rc_key_mass_slots(const rc_ring* r, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                            int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse,
+                            const int32_t* ranges, int32_t n_ranges, float* mass, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (n_ranges < 1) return fail(RC_ERR_ARG, "n_ranges must be >= 1 (got %d)", n_ranges);
+  return key_mass_impl(r, q, n_q, q_pos0, q_block0, q_block_len, cache_bias, softmax_scale, lse, ranges, n_ranges,
+                       mass, workspace, workspace_bytes, stream);
 }
 
 rc_status rc_ring_advance(rc_ring* r, int32_t n) {

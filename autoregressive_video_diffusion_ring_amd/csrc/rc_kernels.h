@@ -52,11 +52,14 @@ int attention_splits(const RingView& r, int n_q);
 size_t attention_workspace_bytes(const RingView& r, int n_q);
 hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStream_t s);
 
-// Attention mass per head and slot (memory.hip).
+// Attention mass per head and slot (memory.hip), optionally only for the
+// slots of up to kMassRanges ranges [lo, hi) (ranges: lo, hi pairs on the
+// host; n_ranges 0 = every slot).
+constexpr int kMassRanges = 4;
 bool key_mass_supported(int kv, int d);
 size_t key_mass_workspace_bytes(const RingView& r, int n_q);
-hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* lse, float* mass,
-                           hipStream_t s);
+hipError_t launch_key_mass(const RingView& r, const AttnCall& c, const float* lse, float* mass, const int* ranges,
+                           int n_ranges, hipStream_t s);
 
 // Scored content memory (memory.hip): before a write of n_new tokens at
 // `head`, keep the best of the memory's tokens and the history tokens the

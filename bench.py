@@ -34,9 +34,11 @@ ramps 0, -2, -4, -2, 0) and prints one JSON line with the sustained ms/chunk
 (median and p99).  ``--anchor A`` makes those rings anchored: the first A
 tokens (A = 757: the first chunk) stay pinned and the other slots slide;
 ``--memory M`` adds a scored content memory of M slots: the last pass of
-every chunk also computes each layer's key mass (rc_key_mass, from that
-pass's queries and lse), and the next chunk's first write keeps the best
-tokens in the memory (rc_cache_write_scored, diversity ``--diversity``).
+every chunk also computes each layer's key mass for the next write's
+candidates (rc_key_mass_slots over the occupied memory slots and the slots
+that write overwrites, from that pass's queries and lse), and the next
+chunk's first write keeps the best tokens in the memory
+(rc_cache_write_scored, diversity ``--diversity``).
 """
 from __future__ import annotations
 
@@ -287,12 +289,15 @@ def longrun(n_chunks: int, anchor: int = 0, memory: int = 0, diversity: float = 
     plain ring; an anchor, older still, moves below 0 with them); the cache
     bias follows ten ramps.  With anchor > 0 every ring pins its first
     `anchor` tokens; with memory > 0 every ring has a scored content memory
-    of that many slots, scored by the key mass of each chunk's last pass."""
+    of that many slots, scored by the key mass of each chunk's last pass
+    (computed for the next scored write's candidates only: the occupied
+    memory slots and the slots that write overwrites)."""
     import torch
 
     from autoregressive_video_diffusion_ring_amd import (Ring, rc_cache_write, rc_cache_write_scored,
                                                          rc_cache_write_scored_workspace_bytes, rc_chunk_attention,
-                                                         rc_key_mass, rc_key_mass_workspace_bytes, rc_ring_advance)
+                                                         rc_key_mass_slots, rc_key_mass_workspace_bytes,
+                                                         rc_ring_advance)
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
@@ -327,6 +332,17 @@ def longrun(n_chunks: int, anchor: int = 0, memory: int = 0, diversity: float = 
             score = memory and p == PASSES - 1
             if score:
                 masses.zero_()
+                # the next scored write's candidates: the occupied memory slots
+                # and the slots that write overwrites (all rings move together)
+                s0 = structs[0]
+                E = N - memory
+                nh = s0.head + NEW
+                nh = nh if nh < E else anchor + nh - E
+                ranges = [(nh, min(nh + NEW, E))]
+                if nh + NEW > E:
+                    ranges.append((anchor, anchor + nh + NEW - E))
+                if s0.n_mem > 0:
+                    ranges.append((E, E + s0.n_mem))
             for layer in range(LAYERS):
                 q, k, v = pool[(240 * t + 60 * p + layer) % POOL]
                 sample = layer == 0 and t >= 8
@@ -347,8 +363,8 @@ def longrun(n_chunks: int, anchor: int = 0, memory: int = 0, diversity: float = 
                     if sample:
                         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                         b0.record(stream)
-                    rc_key_mass(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, lse, masses[layer], ws_m, nb_m,
-                                sptr)
+                    rc_key_mass_slots(structs[layer], q, NEW, pos0, t, NEW, bias, 0.0, lse, ranges, masses[layer],
+                                      ws_m, nb_m, sptr)
                     if sample:
                         b1.record(stream)
                         ev_mass.append((b0, b1))

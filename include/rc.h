@@ -240,6 +240,22 @@ rc_status rc_key_mass(const rc_ring* ring, const void* q, int32_t n_q, int32_t q
                       int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse, float* mass,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rc_key_mass for the slots of n_ranges (1..4) slot ranges only: the scored
+ * write reads the scores of its candidates alone (the memory slots and the
+ * slots the next write overwrites), so only those need the mass.
+ *   ranges     host int32 pairs lo, hi with 0 <= lo < hi <= n_slots; the
+ *              slots lo .. hi-1 of each range get their mass added exactly as
+ *              rc_key_mass would add it (the same sums, bit for bit); every
+ *              other entry of mass is left untouched
+ * Arguments otherwise, workspace and errors as rc_key_mass; a bad range or
+ * count is RC_ERR_ARG.
+ */
+rc_status rc_key_mass_slots(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0, int32_t q_block0,
+                            int32_t q_block_len, float cache_bias, float softmax_scale, const float* lse,
+                            const int32_t* ranges, int32_t n_ranges, float* mass, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Workspace rc_key_mass needs for n_q queries (0 for a bad ring or n_q). */
 size_t rc_key_mass_workspace_bytes(const rc_ring* ring, int32_t n_q);
 

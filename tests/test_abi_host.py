@@ -266,6 +266,21 @@ def test_key_mass_checks():
     assert call(ring=fake_ring(100, kv=RC_BF16)) == RC_ERR_UNSUPPORTED
     assert L.rc_key_mass_workspace_bytes(ctypes.byref(fake_ring(100, kv=RC_BF16)), 70) == 0
 
+    def call_slots(ranges, n=None, lse=FAKE):
+        flat = [v for pair in ranges or [] for v in pair]
+        arr = (ctypes.c_int32 * max(len(flat), 1))(*flat) if ranges is not None else None
+        count = len(flat) // 2 if n is None else n
+        return L.rc_key_mass_slots(ctypes.byref(r), FAKE, 70, 0, 0, 70, 0.0, 0.0, lse, arr, count, FAKE, FAKE,
+                                   need, None)
+    assert call_slots([]) == RC_ERR_ARG                         # no range
+    assert call_slots([(0, 10)] * 5) == RC_ERR_ARG              # more than four
+    assert call_slots(None, n=1) == RC_ERR_ARG                  # NULL ranges
+    assert call_slots([(10, 10)]) == RC_ERR_ARG                 # empty range
+    assert call_slots([(-1, 10)]) == RC_ERR_ARG
+    assert call_slots([(90, 101)]) == RC_ERR_ARG                # past n_slots
+    assert "range 0" in L.rc_last_error().decode()
+    assert call_slots([(0, 10)], lse=0) == RC_ERR_ARG           # the rc_key_mass checks still apply
+
 
 def test_attention_ex_checks():
     L = lib()

@@ -123,6 +123,34 @@ def test_key_mass_multiblock_ragged():
     assert np.allclose(got.sum(axis=1), 150.0, rtol=2e-2)
 
 
+def test_key_mass_slot_ranges():
+    """rc_key_mass_slots: the mass of the listed slots equals rc_key_mass's,
+    bit for bit, and every other entry keeps its old value.  Ranges as the
+    scored write uses them (memory slots and a write range that wraps), on a
+    wrapped ring with empty slots."""
+    banner("key mass over slot ranges: fp8 d=128 N=1500 H=3, ranges that wrap and straddle groups")
+    rng = np.random.default_rng(54)
+    N, H, d = 1500, 3, 128
+    g = Ring(N, H, d, "fp8", 10000.0, first_slot=1300, device=DEV)
+    for b, (n, p0) in enumerate([(400, 0), (500, 400), (300, 900)]):
+        kt, _ = inputs(rng, "fp8", (n, H, d))
+        vt, _ = inputs(rng, "fp8", (n, H, d))
+        g.write(kt, vt, p0, b)
+        g.advance(n)
+    qt, _ = inputs(rng, "fp8", (300, H, d))
+    lse = torch.empty((H, 300), dtype=torch.float32, device=DEV)
+    g.attention(qt, 900, 2, 300, -0.5, lse=lse)
+    full = g.key_mass(qt, 900, 2, 300, -0.5, lse)
+    for ranges in ([(1300, 1500), (0, 37)], [(5, 6)], [(0, 1500)], [(511, 513), (1000, 1024), (1100, 1200)]):
+        sentinel = torch.full_like(full, 7.0)
+        got = g.key_mass(qt, 900, 2, 300, -0.5, lse, mass=sentinel.clone(), ranges=ranges)
+        inside = torch.zeros(full.shape[1], dtype=torch.bool, device=DEV)
+        for lo, hi in ranges:
+            inside[lo:hi] = True
+        assert torch.equal(got[:, inside], full[:, inside] + 7.0), ranges
+        assert torch.all(got[:, ~inside] == 7.0), ranges
+
+
 def test_key_mass_stream_full_size():
     """The streaming shape (757 queries over 5,788 FP8 slots, 40 heads); the
     oracle checks four of the heads."""
