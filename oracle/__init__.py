@@ -15,6 +15,9 @@ What it computes (all in float64 unless a stored format fixes the precision):
 * ``attention`` -- block-causal chunk attention of new queries over every
                    cached slot with the additive cache bias.
 * ``schedule``  -- the long-run schedule: position resets and bias ramps.
+* ``memory``    -- per-key attention mass and the scored content memory's
+                   greedy selection (top-M with diminishing returns per block).
+* ``projection``-- the QKV projection on FP8 operands that feeds the write.
 
 The method is described in: Runway Characters: Serving a 57B Video Diffusion
 Transformer for Real-Time Conversation (abstract) -- ring cache, RoPE and FP8
@@ -22,7 +25,9 @@ quantisation once per write, delta rotation on position reset; video-conductor
 (daydream), "Plastic Windows" -- lowering the cache attention bias during
 prompt transitions; StreamLTX project page (Training) and "Why Live Video
 Generation Still Struggles With Timing" (transcript) -- bidirectional inside a
-block, backward-only across blocks.
+block, backward-only across blocks, anchors plus a sliding window; StreamLTX
+("Why a long take does not slow down") -- anchor, scored content memory and
+FIFO eviction.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.  The one
 reading that no pin can fix is the scale of the pages' "bias=0.3" (parity
