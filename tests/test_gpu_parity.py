@@ -379,6 +379,36 @@ def test_joint_av_four_paths():
         print(f"  {name}: ok", flush=True)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_per_query_blocks(d):
+    """rc_chunk_attention_ex on an FP8 ring with RoPE: unequal blocks (100,
+    170, 130, 140 tokens, so 32-query waves straddle block edges), every
+    token's query carrying its block id; the block-causal mask with bias -0.4
+    on earlier blocks, and the same-block mask.  All rows against the oracle
+    over the GPU's own cache."""
+    banner(f"fp8 d={d}: per-query blocks 100/170/130/140, both masks, bias -0.4")
+    rng = np.random.default_rng(57)
+    lens = [100, 170, 130, 140]
+    N, H = 600, 2
+    g, o = make_pair(N, H, d, "fp8", 10000.0)
+    pos = 0
+    for b, n in enumerate(lens):
+        write_both(g, o, rng, n, pos, b)
+        if b < len(lens) - 1:
+            g.advance(n)
+            o.advance(n)
+        pos += n
+    n_q = sum(lens)
+    qt, q = inputs(rng, "fp8", (n_q, H, d))
+    ids = np.repeat(np.arange(len(lens)), lens).astype(np.int32)
+    orc = oracle_from_gpu(g, 10000.0)
+    for same in (False, True):
+        out = g.attention(qt, 0, 0, None, -0.4, q_block=torch.from_numpy(ids).to(DEV), same_block=same)
+        ref, _ = ring_attention(orc, q, 0, 0, 1, -0.4, q_blocks=ids, mask="same" if same else "causal")
+        assert_attention_close(out, ref, "fp8")
+        print(f"  {'same-block' if same else 'block-causal'}: ok", flush=True)
+
+
 def test_joint_av_six_paths_first_block():
     """All six paths of the joint block with the first block one frame
     longer (1,536 video / 26 audio tokens, then 1,152 / 25) and three prompt
