@@ -349,9 +349,18 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
   constexpr int LPR = D / EPT;          // lanes per row
   constexpr int RPB = kThreads / LPR;   // rows per block pass
   const int lane = threadIdx.x % LPR;
+  // A wave needs only the d/2 factor pairs: each lane computes pair
+  // (its lane index mod d/2) and takes the EPT/2 pairs of its row piece from
+  // the lanes that hold them.
+  static_assert(D / 2 <= kWave, "one factor pair per lane");
+  float c1, s1;
+  rope_cs(rope, (threadIdx.x % kWave) % (D / 2), delta, &c1, &s1);
   float cc[EPT / 2], ss[EPT / 2];
 #pragma unroll
-  for (int e = 0; e < EPT / 2; ++e) rope_cs(rope, lane * (EPT / 2) + e, delta, &cc[e], &ss[e]);
+  for (int e = 0; e < EPT / 2; ++e) {
+    cc[e] = __shfl(c1, lane * (EPT / 2) + e, kWave);
+    ss[e] = __shfl(s1, lane * (EPT / 2) + e, kWave);
+  }
   const int rows = r.H * r.N;
   const int stride = gridDim.x * RPB;
   for (int row0 = blockIdx.x * RPB + threadIdx.x / LPR; row0 < rows; row0 += kRotRows * stride) {
