@@ -427,6 +427,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--no-joint-av", action="store_true", help="skip the joint audio-video paths")
+    ap.add_argument("--joint-av-only", action="store_true",
+                    help="time only the joint audio-video paths and print their line")
     ap.add_argument("--longrun", type=int, default=0, metavar="K",
                     help="run K chunks of the long-run schedule instead and print that line")
     ap.add_argument("--anchor", type=int, default=0, metavar="A",
@@ -454,6 +456,9 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.joint_av_only:
+        print(json.dumps({"joint_av": joint_av(dev, stream)}), flush=True)
+        return 0
     sptr = stream.cuda_stream
     gen = torch.Generator(device=dev)
     gen.manual_seed(1)
