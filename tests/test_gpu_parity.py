@@ -112,6 +112,29 @@ def test_write_wrap_and_rewrite(head0):
     assert g.state() == o.state()
 
 
+@pytest.mark.parametrize("kv,d,H,head0", [("fp8", 128, 40, 1234), ("bf16", 64, 8, 5787)])
+def test_write_whole_ring_one_call(kv, d, H, head0):
+    """The largest write: n_new = N tokens in one call from a head inside the
+    ring, so the write wraps and every slot is overwritten; then attention of
+    the chunk's last 96 queries over all N slots (one block, all visible)."""
+    banner(f"write: whole ring in one call, {kv} d={d} N=5788 H={H} from head {head0}; attention over it")
+    rng = np.random.default_rng(WORKLOADS["wrap"].seed + 11)
+    N = 5788
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=head0)
+    write_both(g, o, rng, N, 2000, 0)
+    c = gpu_cache(g)
+    compare_cache(c, o, kv)
+    assert (c["slot_block"] == 0).all()
+    assert np.array_equal(c["slot_pos"][(head0 + np.arange(N)) % N], 2000 + np.arange(N))
+    qt, q = inputs(rng, kv, (96, H, d))
+    out = g.attention(qt, 2000 + N - 96, 0, 96, -0.5)
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 2000 + N - 96, 0, 96, -0.5)
+    assert_attention_close(out, ref, kv)
+    g.advance(N)
+    o.advance(N)
+    assert g.state() == o.state()
+
+
 @pytest.mark.parametrize("kv,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("fp8", 64)])
 def test_write_other_formats(kv, d):
     banner(f"write: {kv} d={d} ragged chunks with wrap")
