@@ -189,6 +189,40 @@ def test_anchor_ring_stream(kv, d, N, A, n, H, chunks):
 
 
 # ------------------------------------------------------------------ rerotate
+@pytest.mark.parametrize("kv,d", [("fp8", 128), ("bf16", 64), ("f32", 64)])
+def test_rerotate_zero_large_and_partial(kv, d):
+    """Degenerate and extreme shifts on a partly filled, wrapped ring (300
+    slots, 130 written from slot 250): delta 0 (the identity rotation, up to
+    requantisation), then +200,000 positions; every occupied slot matches the
+    oracle, and the 170 empty slots keep their bytes and positions."""
+    banner(f"rerotate: {kv} d={d} N=300 H=3, 130 of 300 slots written from slot 250; delta 0 then +200000")
+    rng = np.random.default_rng(33)
+    N, H = 300, 3
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=250)
+    write_both(g, o, rng, 130, 70, 4)
+    g.advance(130)
+    o.advance(130)
+    c0 = gpu_cache(g)
+    empty = c0["slot_block"] == -1
+    assert int(empty.sum()) == 170
+    for delta in (0, 200_000):
+        ref = oracle_from_gpu(g, 10000.0)
+        g.rerotate(delta)
+        ref.rerotate(delta)
+        o.rerotate(delta)
+        c = gpu_cache(g)
+        compare_cache(c, ref, kv)
+        assert c["state"] == o.state()
+        assert np.array_equal(c["k"][:, empty], c0["k"][:, empty])
+        assert np.array_equal(c["slot_pos"][empty], c0["slot_pos"][empty])
+        if kv == "fp8":
+            assert np.array_equal(c["k_scale"][:, empty], c0["k_scale"][:, empty])
+    # positions moved by the sum of the shifts
+    assert np.array_equal(c["slot_pos"][~empty], c0["slot_pos"][~empty] + 200_000)
+    # V is never touched by a re-rotation
+    assert np.array_equal(c["v"], c0["v"])
+
+
 def test_rerotate_wrap_reset():
     banner("rerotate: head 5400 (wrapped current chunk), delta -3000 over all slots")
     head0 = (5400 - 5031) % 5788
