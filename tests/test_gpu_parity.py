@@ -276,6 +276,32 @@ def test_attention_ragged_multiblock(kv, d):
     assert_attention_close(out, ref2, kv)
 
 
+@pytest.mark.parametrize("kv,d", [("fp8", 128), ("bf16", 64), ("f32", 64)])
+def test_attention_single_query_and_softmax_scale(kv, d):
+    """One query (the smallest call), then 70 queries in two blocks with
+    softmax scales other than 1/sqrt(d) (0.05 and 0.5), over a wrapped ring
+    of three blocks with a bias on the earlier ones."""
+    banner(f"attention: {kv} d={d} N=200 H=2, one query; then softmax scale 0.05 and 0.5")
+    rng = np.random.default_rng(44)
+    N, H = 200, 2
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=170)
+    for b, (n, p0) in enumerate([(64, 500), (64, 564), (40, 628)]):
+        write_both(g, o, rng, n, p0, b)
+        g.advance(n)
+        o.advance(n)
+    qt, q = inputs(rng, kv, (1, H, d))
+    out = g.attention(qt, 667, 2, 1, -0.3)
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 667, 2, 1, -0.3)
+    assert_attention_close(out, ref, kv)
+    qt, q = inputs(rng, kv, (70, H, d))
+    for scale in (0.05, 0.5):
+        out = g.attention(qt, 600, 1, 35, -0.3, scale)
+        ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 600, 1, 35, -0.3, scale)
+        assert_attention_close(out, ref, kv)
+        ref2, _ = ring_attention(o, q, 600, 1, 35, -0.3, scale)
+        assert_attention_close(out, ref2, kv)
+
+
 def test_attention_zero_rows_and_scale_spread():
     """Degenerate and extreme rows: all-zero K rows (scale 0), all-zero V rows
     (scale 0: the row still carries its softmax weight, so the sum must count
