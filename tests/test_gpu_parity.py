@@ -148,6 +148,35 @@ def test_write_other_formats(kv, d):
     compare_cache(gpu_cache(g), o, kv)
 
 
+@pytest.mark.parametrize("kv,d", [("fp8", 128), ("fp8", 64), ("bf16", 128), ("f32", 64)])
+def test_write_single_tokens(kv, d):
+    """One-token writes: a chunk of one slot inside a 32-slot group, at the
+    ring's last slot, then at slot 0 after the wrap, with two passes over the
+    same token; each compared with the oracle, neighbours untouched."""
+    banner(f"write: {kv} d={d} single tokens at slots 37, 199, 0 (N=200, H=3)")
+    rng = np.random.default_rng(12)
+    N, H = 200, 3
+    g, o = make_pair(N, H, d, kv, 10000.0, first_slot=37)
+    write_both(g, o, rng, 1, 5, 0)
+    compare_cache(gpu_cache(g), o, kv)
+    g.advance(1)
+    o.advance(1)
+    # move the head to the last slot with a 161-token chunk, then one token there
+    write_both(g, o, rng, 161, 6, 1)
+    g.advance(161)
+    o.advance(161)
+    assert g.state()[0] == 199
+    for blk, pos in ((2, 167), (3, 168)):
+        for _ in range(2):  # two denoising passes over the same token
+            write_both(g, o, rng, 1, pos, blk)
+            compare_cache(gpu_cache(g), o, kv)
+        g.advance(1)
+        o.advance(1)
+    c = gpu_cache(g)
+    assert c["slot_block"][199] == 2 and c["slot_block"][0] == 3 and c["slot_block"][1] == -1
+    assert g.state() == o.state()
+
+
 @pytest.mark.parametrize("kv,d,N,A,n,H,chunks", [
     ("fp8", 128, 300, 50, 77, 3, 9),       # chunk 0 straddles the anchor; ragged wraps to slot 50
     ("bf16", 64, 200, 64, 40, 3, 10),
