@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
 
 // Delta re-rotation of every occupied row.  A row of K (d elements) is
 // handled by LPR lanes with 16 bytes each; a thread takes kRotRows rows whose
-// loads are all issued before any arithmetic.
+// loads are all issued before any of the rows' arithmetic.
 constexpr int kRotRows = 4;
 
 template <int KV, int D>
