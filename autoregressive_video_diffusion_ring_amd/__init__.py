@@ -8,7 +8,8 @@ kernels behind the C ABI.  The entry points keep the C names:
     rc_ring_advance, rc_attention_workspace_bytes, rc_debug_visibility,
     rc_key_mass, rc_key_mass_slots, rc_key_mass_workspace_bytes,
     rc_cache_write_scored, rc_cache_write_scored_workspace_bytes,
-    rc_chunk_attention_ex, rc_qkv_project_write, rc_qkv_workspace_bytes
+    rc_chunk_attention_ex, rc_qkv_project_write, rc_qkv_workspace_bytes,
+    rc_set_attention_precision
 
 and ``Ring`` owns a ring's device buffers (torch tensors) and its rc_ring
 struct.  See include/rc.h for the meaning of every argument.
@@ -19,8 +20,8 @@ import ctypes
 
 import torch
 
-from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, RC_MASK_SAME_BLOCK, RcError, RcRing,
-                   check, lib)
+from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, RC_MASK_SAME_BLOCK,
+                   RC_PRECISION_AUTO, RC_PRECISION_ONE_TERM, RC_PRECISION_TWO_TERM, RcError, RcRing, check, lib)
 
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
@@ -28,7 +29,8 @@ __all__ = [
     "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_slots", "rc_key_mass_workspace_bytes",
     "rc_cache_write_scored",
     "rc_cache_write_scored_workspace_bytes", "rc_chunk_attention_ex", "RC_MASK_BLOCK_CAUSAL", "RC_MASK_SAME_BLOCK",
-    "rc_qkv_project_write", "rc_qkv_workspace_bytes",
+    "rc_qkv_project_write", "rc_qkv_workspace_bytes", "rc_set_attention_precision", "RC_PRECISION_AUTO",
+    "RC_PRECISION_TWO_TERM", "RC_PRECISION_ONE_TERM",
 ]
 
 
@@ -109,6 +111,10 @@ def rc_qkv_project_write(ring: RcRing, x, n: int, C: int, w, w_scale, pos0: int,
 
 def rc_qkv_workspace_bytes(n: int, C: int) -> int:
     return lib().rc_qkv_workspace_bytes(n, C)
+
+
+def rc_set_attention_precision(mode: int) -> None:
+    check(lib().rc_set_attention_precision(mode))
 
 
 def rc_attention_workspace_bytes(ring: RcRing, n_q: int) -> int:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librc.so")
 
-SOURCES = ["rc_host.cpp", "cache_write.hip", "chunk_attn.hip", "memory.hip", "qkv_write.hip"]
+SOURCES = ["rc_host.cpp", "cache_write.hip", "chunk_attn.hip", "attn_fp8.hip", "memory.hip", "qkv_write.hip"]
 
 # Packed fp32 instructions are disabled for device code: they are generated
 # only from ordinary float code and are not needed on any path here.
@@ -35,9 +35,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librc.so)")
 
 
-# The attention kernel handles no NaN inputs specially; without NaN
-# semantics its maxima compile to plain v_max3 instructions.
-EXTRA = {"chunk_attn.hip": ["-fno-honor-nans"]}
+# The attention kernels handle no NaN inputs specially; without NaN
+# semantics their maxima compile to plain v_max3 instructions.
+EXTRA = {"chunk_attn.hip": ["-fno-honor-nans"], "attn_fp8.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

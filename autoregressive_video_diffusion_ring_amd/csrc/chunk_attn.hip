@@ -964,6 +964,7 @@ hipError_t attn_impl(const RingView& r, const AttnCall& c, int splits, hipStream
 bool attention_supported(int kv, int d) { return !(kv == KV_F32 && d == 128); }
 
 int attention_splits(const RingView& r, int n_q) {
+  if (r.kv == KV_FP8) return fp8_attention_splits(r, n_q);
   const int n_qt = (n_q + kQT - 1) / kQT;
   const int n_tiles = (r.N + kKT - 1) / kKT;
   const int items = n_qt * r.H;
@@ -984,9 +985,8 @@ hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStrea
   int splits = attention_splits(r, c.n_q);
   if (splits > 1 && (c.workspace == nullptr || c.workspace_bytes < attention_workspace_bytes(r, c.n_q)))
     splits = 1;
+  if (r.kv == KV_FP8) return launch_fp8_attention(r, c, splits, s);
   switch (r.kv * 1000 + r.d) {
-    case KV_FP8 * 1000 + 128: return attn_impl<KV_FP8, 128>(r, c, splits, s);
-    case KV_FP8 * 1000 + 64: return attn_impl<KV_FP8, 64>(r, c, splits, s);
     case KV_BF16 * 1000 + 128: return attn_impl<KV_BF16, 128>(r, c, splits, s);
     case KV_BF16 * 1000 + 64: return attn_impl<KV_BF16, 64>(r, c, splits, s);
     case KV_F32 * 1000 + 64: return attn_impl<KV_F32, 64>(r, c, splits, s);

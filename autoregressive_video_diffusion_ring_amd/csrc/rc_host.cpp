@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -38,6 +39,7 @@ static_assert(offsetof(rc_ring, n_mem) == 100 && sizeof(rc_ring) == 104, "rc_rin
 namespace {
 
 thread_local std::string g_err;
+std::atomic<int> g_precision{RC_PRECISION_AUTO};
 
 rc_status fail(rc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 rc_status fail(rc_status st, const char* fmt, ...) {
@@ -170,7 +172,7 @@ extern "C" {
 
 int32_t rc_ring_v_ld(int32_t n_slots) {
   if (n_slots < 1) return 0;
-  return (n_slots + 63) / 64 * 64;
+  return (n_slots + 127) / 128 * 128;
 }
 
 rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int32_t kv_dtype, size_t out[6]) {
@@ -294,6 +296,13 @@ rc_status rc_cache_rerotate(rc_ring* r, int32_t delta, void* stream) {
   return ok();
 }
 
+rc_status rc_set_attention_precision(int32_t mode) {
+  if (mode != RC_PRECISION_AUTO && mode != RC_PRECISION_TWO_TERM && mode != RC_PRECISION_ONE_TERM)
+    return fail(RC_ERR_ARG, "unknown attention precision mode %d", mode);
+  g_precision.store(mode);
+  return ok();
+}
+
 size_t rc_attention_workspace_bytes(const rc_ring* r, int32_t n_q) {
   if (check_ring(r) != RC_OK || n_q < 1) return 0;
   return rc::attention_workspace_bytes(view(r), n_q);
@@ -324,6 +333,7 @@ rc_status rc_chunk_attention_ex(const rc_ring* r, const void* q, int32_t n_q, in
                  workspace_bytes};
   c.q_block_ids = q_block;
   c.same_block = mask == RC_MASK_SAME_BLOCK;
+  c.precision = g_precision.load();
   hipError_t e = rc::launch_chunk_attention(view(r), c, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk attention");
   return ok();

@@ -43,6 +43,7 @@ struct AttnCall {
   size_t workspace_bytes;
   const int32_t* q_block_ids = nullptr;  // [n_q] or null (q_block0 + i / q_block_len)
   int same_block = 0;                    // 1: visible iff slot block == query block
+  int precision = 0;                     // FP8 rings: 0 by key count, 1 two-term Q and P, 2 one-term
 };
 
 // Whether an attention kernel is built for this KV format and head size.
@@ -51,6 +52,9 @@ bool attention_supported(int kv, int d);
 int attention_splits(const RingView& r, int n_q);
 size_t attention_workspace_bytes(const RingView& r, int n_q);
 hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStream_t s);
+// FP8 rings (attn_fp8.hip): key splits for n_q queries and the launch.
+int fp8_attention_splits(const RingView& r, int n_q);
+hipError_t launch_fp8_attention(const RingView& r, const AttnCall& c, int splits, hipStream_t s);
 
 // Attention mass per head and slot (memory.hip), optionally only for the
 // slots of up to kMassRanges ranges [lo, hi) (ranges: lo, hi pairs on the

@@ -107,7 +107,8 @@ typedef struct rc_ring {
   int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem;
 } rc_ring;
 
-/* Leading dimension of the transposed V buffer: N rounded up to 64. */
+/* Leading dimension of the transposed V buffer: N rounded up to 128 (a whole
+   number of the attention's 128-slot tiles). */
 int32_t rc_ring_v_ld(int32_t n_slots);
 
 /*
@@ -208,6 +209,30 @@ rc_status rc_chunk_attention_ex(const rc_ring* ring, const void* q, int32_t n_q,
                                 const int32_t* q_block, int32_t q_block0, int32_t q_block_len, int32_t mask,
                                 float cache_bias, float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Operand precision of the attention on FP8 rings, for the whole process (a
+ * checking and measurement control; the default needs no call).  The FP8
+ * attention quantises the rotated queries with one power-of-two scale per
+ * (query, head) and the probabilities per score; each FP8 term keeps 3
+ * mantissa bits, and the output error they cause falls like one over the
+ * square root of the effective number of keys a query sees (Runway
+ * Characters, abstract: FP8 KV cache; the rest of the attention's arithmetic
+ * is the block-causal softmax of rc_chunk_attention).
+ *   RC_PRECISION_AUTO      (0, default) per workgroup of 128 queries of one
+ *                          head: one FP8 term for Q and for P when all its
+ *                          queries lie in one block b and
+ *                          (n_b + n_<b w)^2 / (n_b + n_<b w^2) >= 2048, where
+ *                          n_b / n_<b count the slots of block b / of earlier
+ *                          blocks and w = exp(cache_bias) (for the same-block
+ *                          mask n_<b = 0); two terms (the codes of the residual
+ *                          at 1/16 of the scale added) otherwise
+ *   RC_PRECISION_TWO_TERM  (1) two terms everywhere
+ *   RC_PRECISION_ONE_TERM  (2) one term everywhere
+ * RC_ERR_ARG for any other mode.  Calls already enqueued are not affected.
+ */
+typedef enum { RC_PRECISION_AUTO = 0, RC_PRECISION_TWO_TERM = 1, RC_PRECISION_ONE_TERM = 2 } rc_precision;
+rc_status rc_set_attention_precision(int32_t mode);
 
 /* Workspace that lets rc_chunk_attention use its full key split for n_q queries. */
 size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);

@@ -87,16 +87,14 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
 
 
-# Attention tolerances by KV storage: (max-abs, rel-L2).  rel-L2 is the
-# shape-independent gate: FP8 Q and P each round to 3 mantissa bits (about
-# 2-4% relative error in the output), bf16 to 8, f32 to 24.  The max-abs
-# 2e-2 bound is stated for unit-variance inputs at the streaming shape
-# (5,788 visible slots, max |out| about 0.1).  The FP8 error is relative, so
-# for the FP8 path the absolute bound is scaled by max|out| / 0.1 when the
-# outputs are larger than at that shape (fewer visible slots); at the
-# streaming shape it is exactly 2e-2.
+# Attention tolerances by KV storage: (max-abs, rel-L2).  The max-abs bound
+# 2e-2 is the one stated for unit-variance inputs, at every shape; rel-L2 is
+# a second gate that stays meaningful when outputs are small (at 5,788
+# visible slots max |out| is about 0.1, where a bias or mask bug moves
+# outputs by less than 2e-2 but by 20-40 % rel-L2).  FP8 Q and P round to 3
+# mantissa bits per term (one term at many keys, two below 2,048 effective
+# keys), bf16 to 8, f32 to 24.
 ATTN_TOL = {"fp8": (2e-2, 6e-2), "bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}
-FP8_REF_MAX = 0.1
 
 
 def assert_attention_close(out_gpu, out_ref, kv: str, rows=None):
@@ -104,8 +102,6 @@ def assert_attention_close(out_gpu, out_ref, kv: str, rows=None):
     if rows is not None:
         g = g[rows]
     mx, rl = ATTN_TOL[kv]
-    if kv == "fp8":
-        mx *= max(1.0, float(np.max(np.abs(out_ref))) / FP8_REF_MAX)
     err = np.max(np.abs(g - out_ref))
     r = rel_l2(g, out_ref)
     assert err <= mx and r <= rl, f"max-abs {err:.3e} (<= {mx}), rel-L2 {r:.3e} (<= {rl})"

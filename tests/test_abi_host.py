@@ -66,10 +66,11 @@ def state(r):
 
 def test_v_ld_and_sizes():
     L = lib()
-    assert [L.rc_ring_v_ld(n) for n in (1, 63, 64, 65, 5788, 11520)] == [64, 64, 64, 128, 5824, 11520]
+    assert [L.rc_ring_v_ld(n) for n in (1, 63, 64, 65, 128, 129, 5788, 11520)] == [128, 128, 128, 128, 128, 256,
+                                                                                  5888, 11520]
     out = (ctypes.c_size_t * 6)()
     assert L.rc_ring_sizes(5788, 40, 128, RC_FP8_E4M3, out) == RC_OK
-    assert list(out) == [40 * 5824 * 128, 40 * 128 * 5824, 40 * 5824 * 4, 40 * 5824 * 4, 5824 * 4, 5824 * 4]
+    assert list(out) == [40 * 5888 * 128, 40 * 128 * 5888, 40 * 5888 * 4, 40 * 5888 * 4, 5888 * 4, 5888 * 4]
     assert L.rc_ring_sizes(96, 2, 64, RC_F32, out) == RC_OK
     assert list(out) == [2 * 128 * 64 * 4, 2 * 64 * 128 * 4, 0, 0, 128 * 4, 128 * 4]
     assert L.rc_ring_sizes(96, 2, 96, RC_BF16, out) == RC_ERR_UNSUPPORTED
