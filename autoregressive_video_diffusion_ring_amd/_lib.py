@@ -28,7 +28,7 @@ class RcRing(ctypes.Structure):
         ("k", c_void_p), ("v", c_void_p), ("k_scale", c_void_p), ("v_scale", c_void_p),
         ("slot_pos", c_void_p), ("slot_block", c_void_p),
         ("head", c_int32), ("n_hist", c_int32), ("n_cur", c_int32), ("cur_pos0", c_int32),
-        ("cur_block", c_int32), ("n_mem", c_int32),
+        ("cur_block", c_int32), ("n_mem", c_int32), ("max_block", c_int32),
     ]
 
 

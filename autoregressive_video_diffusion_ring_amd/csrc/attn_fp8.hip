@@ -34,11 +34,12 @@
 // tau = 8 (log2), so P~ <= 256 stays inside e4m3 and O rescales are rare.
 //
 // Precision.  FP8 Q and P carry 3 mantissa bits each; the output error they
-// cause shrinks like 1 / sqrt(effective number of keys).  A workgroup whose
-// queries see few keys (fewer than kFastMinKeys effective keys, counted in the
-// prologue from the slot blocks and the bias) runs the precise variant: Q and
-// P are each split into two FP8 terms (codes of the value, then codes of the
-// residual at 1/16 of the scale), doubling both MFMA passes.
+// cause shrinks like 1 / sqrt(effective number of keys).  Calls whose queries
+// see few keys (the host bounds the effective key count from the ring state
+// and the bias) run the two-term instantiation: Q and P are each split into
+// two FP8 terms (codes of the value, then codes of the residual at 1/16 of the
+// scale), which doubles both MFMA passes; it handles one 16-query block per
+// pass over the tiles so that its extra operands stay in registers.
 #include <cmath>
 #include <type_traits>
 
@@ -71,13 +72,6 @@ constexpr float kMinA = 0x1p-90f;       // floor of A, so that C stays finite
 constexpr int kOne = 127;               // E8M0 code of 1.0
 constexpr int kLoShift = 4;             // residual terms carry 1/16 of the scale
 
-// Effective number of keys below which a workgroup takes the precise path
-// (two-term Q and P).  With one FP8 term each, unit-variance inputs give an
-// output error of about 0.061 / sqrt(n_eff) (rms); at 2,048 keys that is
-// 1.3e-3 rms, under 1e-2 at the largest deviation over millions of outputs.
-constexpr float kFastMinKeys = 2048.f;
-constexpr int kPreSlots = 16;  // slot blocks each thread loads for the key count (8,192 per workgroup)
-
 struct F8Args {
   const uint8_t* k;
   const uint8_t* v;
@@ -91,10 +85,6 @@ struct F8Args {
   int same_block;
   float bias_log2;   // cache_bias * log2(e) (0 for the same-block mask)
   float scale_log2;  // softmax_scale * log2(e)
-  // weights of same-block and earlier-block keys for the key count, scaled so
-  // that the larger is 1: (1, e^b) for b < 0, (e^-b, 1) otherwise, and squares
-  float ws1, we1, ws2, we2;
-  int precision;     // 0 by key count, 1 always precise, 2 always one-term
   void* out;
   float* lse;
   float* part_o;    // [splits][n_q][H][D] when split
@@ -248,7 +238,8 @@ struct BlkState {
 };
 
 // GEN: per-query block ids and the same-block mask (rc_chunk_attention_ex).
-template <int D, bool GEN>
+// TWO: two FP8 terms for Q and P (one query block per pass over the tiles).
+template <int D, bool GEN, bool TWO>
 __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   using T = Tile<D>;
   constexpr int NDB = D / 16;       // d blocks of the output
@@ -257,7 +248,6 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t st1[Lds<D>::stage];
   __shared__ __attribute__((aligned(16))) float fac0[Lds<D>::fac];
   __shared__ __attribute__((aligned(16))) float fac1[Lds<D>::fac];
-  __shared__ int red[4 * kWaves];
   __shared__ double rev_lds[64];  // RoPE frequencies in revolutions per position
 
   asm volatile("" ::"s"(a.n_qt), "s"(a.n_splits), "s"(a.tiles_per_split), "s"(a.n_tiles), "s"(a.remap),
@@ -299,15 +289,22 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     const int r = p / 8, cp = p % 8;
     v_off[j] = static_cast<uint32_t>(r * a.v_ld + ((cp ^ v_swz(r)) << 4));
   }
-  auto issue = [&](uint8_t* stage, int li) __attribute__((always_inline)) {
+  // the j-th of this wave's T::dma_instr direct loads of tile li (K blocks first)
+  auto issue_j = [&](uint8_t* stage, int li, int j) __attribute__((always_inline)) {
     const int tile = has_tile(li, kh) ? tile_of(li, kh) : t_safe;
     uint8_t* buf = stage + kh * T::bytes;
-    const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + static_cast<size_t>(tile) * kT) * D;
-    const uint8_t* vb = a.v + static_cast<size_t>(h) * D * a.v_ld + static_cast<size_t>(tile) * kT;
+    if (j < T::k_instr) {
+      const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + static_cast<size_t>(tile) * kT) * D;
+      dma16(kb + k_off[j], buf + (wq * T::k_instr + j) * 1024);
+    } else {
+      const int jv = j - T::k_instr;
+      const uint8_t* vb = a.v + static_cast<size_t>(h) * D * a.v_ld + static_cast<size_t>(tile) * kT;
+      dma16(vb + v_off[jv], buf + T::v_off + (wq * T::v_instr + jv) * 1024);
+    }
+  };
+  auto issue = [&](uint8_t* stage, int li) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < T::k_instr; ++j) dma16(kb + k_off[j], buf + (wq * T::k_instr + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < T::v_instr; ++j) dma16(vb + v_off[j], buf + T::v_off + (wq * T::v_instr + j) * 1024);
+    for (int j = 0; j < T::dma_instr; ++j) issue_j(stage, li, j);
   };
 
   // ---- per-slot metadata for the factor tables.  Wave f of key half 0
@@ -360,15 +357,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     my_qb[b] = (GEN && a.q_block_ids) ? a.q_block_ids[qq] : a.q_block0 + qq / a.q_block_len;
   }
 
-  // ---- loads, in the order they are waited for: the RoPE frequencies, the slot blocks for the
-  //      key count, the metadata of the first two steps, Q, the first tiles
+  // ---- loads, in the order they are waited for: the RoPE frequencies, the
+  //      metadata of the first two steps, Q, the first tiles
   const double rev_lane = wave == 0 && lane < D / 2 ? a.rope.rev[lane] : 0.0;
-  int pre_kb[kPreSlots];
-#pragma unroll
-  for (int i = 0; i < kPreSlots; ++i) {
-    const int s = i * kThreads + tid;
-    pre_kb[i] = s < a.N ? a.slot_block[s] : -1;
-  }
   float m2_ks = 0.f, m2_vs = 0.f;
   int m2_kb = -1;
   if (fac_wave) {
@@ -387,68 +378,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 
   if (wave == 0) rev_lds[lane] = rev_lane;
 
-  // ---- precision of this workgroup: count the keys its queries see.  The
-  //      workgroup takes the one-term path only if all its queries lie in one
-  //      block b and the effective number of keys (n_b + n_<b w)^2 /
-  //      (n_b + n_<b w^2), w = exp(bias), reaches kFastMinKeys.
-  int wg_lo, wg_hi;
-  {
-    int lo = INT32_MAX, hi = INT32_MIN;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      if (q_ok[b]) {
-        lo = min(lo, my_qb[b]);
-        hi = max(hi, my_qb[b]);
-      }
-    lo = wave_minmax_i32<false>(lo);
-    hi = wave_minmax_i32<true>(hi);
-    if (lane == 0) {
-      red[wave] = lo;
-      red[kWaves + wave] = hi;
-    }
-    wait_lgkm0();
-    bare_barrier();
-    wg_lo = red[0];
-    wg_hi = red[kWaves];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      wg_lo = min(wg_lo, red[w]);
-      wg_hi = max(wg_hi, red[kWaves + w]);
-    }
-    int n_same = 0, n_early = 0;
-#pragma unroll
-    for (int i = 0; i < kPreSlots; ++i) {
-      n_same += pre_kb[i] == wg_lo;
-      n_early += pre_kb[i] >= 0 && pre_kb[i] < wg_lo;
-    }
-    for (int s = kPreSlots * kThreads + tid; s < a.N; s += kThreads) {  // rings above 8,192 slots
-      const int bk = a.slot_block[s];
-      n_same += bk == wg_lo;
-      n_early += bk >= 0 && bk < wg_lo;
-    }
-    n_same = wave_sum_i32(n_same);
-    n_early = wave_sum_i32(n_early);
-    if (lane == 0) {
-      red[2 * kWaves + wave] = n_same;
-      red[3 * kWaves + wave] = n_early;
-    }
-  }
   wait_lgkm0();
-  bare_barrier();
-  bool precise;
-  {
-    int n_same = 0, n_early = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      n_same += red[2 * kWaves + w];
-      n_early += red[3 * kWaves + w];
-    }
-    if (GEN && a.same_block) n_early = 0;
-    const float s1 = static_cast<float>(n_same) * a.ws1 + static_cast<float>(n_early) * a.we1;
-    const float s2 = static_cast<float>(n_same) * a.ws2 + static_cast<float>(n_early) * a.we2;
-    const bool enough = wg_lo == wg_hi && s2 > 0.f && s1 * s1 >= kFastMinKeys * s2;
-    precise = a.precision == 1 || (a.precision == 0 && !enough);
-  }
+  bare_barrier();  // the RoPE table is visible
 
   // ---- Q: rotate, scale by a power of two per query, quantise into S's
   //      operands (the blocks S holds; with NB = 1 also the residual codes)
@@ -552,137 +483,31 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 
   const int n_steps = n_local;
 
-  // One tile for the query blocks held in `st` (NB = 2: both, the one-term
+  // One tile for the query blocks held in S (NB = 2: both, the one-term
   // path; NB = 1: one block, the two-term path, which runs the tiles once per
-  // block to keep its extra operands in registers):  S'^T = K Q^T + C,
+  // block to keep its extra operands in registers), half-tile by half-tile
+  // (slot blocks sb = 4ht .. 4ht + 3):  S'^T = K Q^T + C,
   // z = A S' (+ bias) - msub, the stabiliser check, P~ = 2^z with
-  // l += P~ / s_v, O^T += V^T P^T.  `common` tiles (both half-tiles visible
-  // to every query of the wave with one bias value each) take the bias per
-  // half-tile; the others are masked per score from the slots' blocks (one
-  // extra pass over the scores, skipped by branch in the common case).
-  auto tile = [&](auto& S, const uint8_t* buf, const float* tbl, bool common, const bool (&hist)[2])
+  // l += P~ / s_v, and after both halves O^T += V^T P^T.  `common` tiles
+  // (both half-tiles visible to every query of the wave with one bias value
+  // each) take the bias per half-tile; the others are masked per score from
+  // the slots' blocks.  If the second half raises the stabiliser, the first
+  // half's probabilities (already FP8, relative to the old stabiliser) are
+  // multiplied into O before O is rescaled.
+  auto tile = [&](auto& S, const uint8_t* buf, const float* tbl, bool common, const bool (&hist)[2], auto&& dma)
                   __attribute__((always_inline)) {
     constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
     constexpr bool two = NB == 1;
-    v4f s[8][NB];
     // lane bases; slot block sb and d block db only add constants (the
     // swizzles depend on the lane alone), so the reads take immediate offsets
     const uint8_t* kl = buf + k_lane_lo;
     const uint8_t* kh8 = buf + k_lane_hi;
-    const float* tg = tbl + 32 * g;
-#pragma unroll
-    for (int sb = 0; sb < 8; ++sb) {
-      v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (g < NG) {
-        const v4i lo = *reinterpret_cast<const v4i*>(kl + 4 * sb * D);
-        const v4i hi = *reinterpret_cast<const v4i*>(kh8 + 4 * sb * D);
-        kop = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
-      const v4f cin = *reinterpret_cast<const v4f*>(tg + kFacC + 4 * sb);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        s[sb][b] = mfma16(kop, S.qf[b], cin, S.qsc[b]);
-        if constexpr (two) s[sb][b] = mfma16(kop, S.ql[b], s[sb][b], S.qsc_lo[b]);
-      }
-    }
-    const float zb0 = common && hist[0] ? a.bias_log2 : 0.f;
-    const float zb1 = common && hist[1] ? a.bias_log2 : 0.f;
-#pragma unroll
-    for (int sb = 0; sb < 8; ++sb) {
-      const v4f af = *reinterpret_cast<const v4f*>(tg + kFacA + 4 * sb);
-      const float zb = sb < 4 ? zb0 : zb1;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float zadd = zb - S.msub[b];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[sb][b][i] = fmaf(s[sb][b][i], af[i], zadd);
-      }
-    }
-    if (!common) {
-#pragma unroll
-      for (int sb = 0; sb < 8; ++sb) {
-        const v4i kb4 = *reinterpret_cast<const v4i*>(tg + kFacKb + 4 * sb);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int qb = S.qb[b];
-          const int lo_qb = same_block ? qb : 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kb = kb4[i];
-            const int cls = !GEN ? visibility_class(kb, qb)
-                                 : (kb < lo_qb || kb > qb) ? kVisNone : (kb < qb ? kVisBias : kVisPlain);
-            const float z = cls == kVisBias ? s[sb][b][i] + a.bias_log2 : s[sb][b][i];
-            s[sb][b][i] = cls == kVisNone ? -INFINITY : z;
-          }
-        }
-      }
-    }
-    float tmax[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) tmax[b] = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < 8; ++sb)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        tmax[b] = fmaxf(fmaxf(tmax[b], fmaxf(s[sb][b][0], s[sb][b][1])), fmaxf(s[sb][b][2], s[sb][b][3]));
-    if constexpr (NB == 2) {
-      across_groups<true>(tmax[0], tmax[1]);
-    } else {
-      float t1 = tmax[0];
-      across_groups<true>(tmax[0], t1);
-    }
-
-    // raise the stabiliser only when the tile maximum passes it by tau
-    bool raise = false;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) raise = raise || tmax[b] + S.msub[b] > S.m_run[b] + kTau;
-    if (__ballot(raise) != 0ull) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float m_new = fmaxf(S.m_run[b], tmax[b] + S.msub[b]);
-        const float alpha = S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
-        S.l_part[b][0] *= alpha;
-        S.l_part[b][1] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) S.o[db][b] *= alpha;
-        const float shift = m_new == -INFINITY ? 0.f : m_new - S.msub[b];
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb) s[sb][b] -= shift;
-        S.m_run[b] = m_new;
-        S.msub[b] = m_new == -INFINITY ? 0.f : m_new;
-      }
-    }
-
-    // P~ = 2^z, l += P~ / s_v, P~ to FP8 (B operand of P V: byte 4 sb + i)
-    v8i pk[NB];
-#pragma unroll
-    for (int sb = 0; sb < 8; ++sb) {
-      const v4f iv = *reinterpret_cast<const v4f*>(tg + kFacIv + 4 * sb);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[sb][b][i] = __builtin_amdgcn_exp2f(s[sb][b][i]);
-          S.l_part[b][i & 1] = fmaf(s[sb][b][i], iv[i], S.l_part[b][i & 1]);
-        }
-        pk[b][sb] = cvt_fp8x4_over(s[sb][b][0], s[sb][b][1], s[sb][b][2], s[sb][b][3], 0);
-      }
-    }
-
-    // O^T += V^T P^T (reduction over the tile's 128 slots); with two terms
-    // the residual codes of P~ follow as a second pass
     const uint8_t* vl = buf + v_lane_lo;
     const uint8_t* vh = buf + v_lane_hi;
-#pragma unroll
-    for (int pass = 0; pass < (two ? 2 : 1); ++pass) {
-      if (pass == 1) {
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb)
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-            pk[b][sb] = residual_fp8x4(s[sb][b][0], s[sb][b][1], s[sb][b][2], s[sb][b][3], pk[b][sb], 0);
-      }
-      const int psc = pass == 0 ? kOne : kOne - kLoShift;
+    const float* tg = tbl + 32 * g;
+    v8i pk[NB];
+    // O^T += V^T P^T over the tile's 128 slots (pass 1: the residual codes)
+    auto pv = [&](int psc) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v4i lo = *reinterpret_cast<const v4i*>(vl + 16 * db * kT);
@@ -691,7 +516,153 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) S.o[db][b] = mfma16(vop, pk[b], S.o[db][b], psc);
       }
+    };
+    v4f p1[4][NB];  // fp32 probabilities of the first half (two-term path: residual codes)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      v4f s[4][NB];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sb = 4 * ht + j;
+        v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (g < NG) {
+          const v4i lo = *reinterpret_cast<const v4i*>(kl + 4 * sb * D);
+          const v4i hi = *reinterpret_cast<const v4i*>(kh8 + 4 * sb * D);
+          kop = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+        const v4f cin = *reinterpret_cast<const v4f*>(tg + kFacC + 4 * sb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          s[j][b] = mfma16(kop, S.qf[b], cin, S.qsc[b]);
+          if constexpr (two) s[j][b] = mfma16(kop, S.ql[b], s[j][b], S.qsc_lo[b]);
+        }
+        // the next tile's direct loads go out between matrix instructions,
+        // so that their issue (which waits while the load queue is full)
+        // overlaps matrix work
+        if (sb < T::dma_instr) dma(sb);
+      }
+      const float zb = common && hist[ht] ? a.bias_log2 : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4f af = *reinterpret_cast<const v4f*>(tg + kFacA + 4 * (4 * ht + j));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float zadd = zb - S.msub[b];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[j][b][i] = fmaf(s[j][b][i], af[i], zadd);
+        }
+      }
+      if (!common) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v4i kb4 = *reinterpret_cast<const v4i*>(tg + kFacKb + 4 * (4 * ht + j));
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int qb = S.qb[b];
+            const int lo_qb = same_block ? qb : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kb = kb4[i];
+              const int cls = !GEN ? visibility_class(kb, qb)
+                                   : (kb < lo_qb || kb > qb) ? kVisNone : (kb < qb ? kVisBias : kVisPlain);
+              const float z = cls == kVisBias ? s[j][b][i] + a.bias_log2 : s[j][b][i];
+              s[j][b][i] = cls == kVisNone ? -INFINITY : z;
+            }
+          }
+        }
+      }
+      float tmax[2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float t0 = fmaxf(fmaxf(s[0][b][0], s[0][b][1]), s[0][b][2]);
+        float t1 = fmaxf(fmaxf(s[1][b][0], s[1][b][1]), s[1][b][2]);
+        float t2 = fmaxf(fmaxf(s[2][b][0], s[2][b][1]), s[2][b][2]);
+        float t3 = fmaxf(fmaxf(s[3][b][0], s[3][b][1]), s[3][b][2]);
+        t0 = fmaxf(fmaxf(t0, s[0][b][3]), s[1][b][3]);
+        t2 = fmaxf(fmaxf(t2, s[2][b][3]), s[3][b][3]);
+        tmax[b] = fmaxf(fmaxf(t0, t1), fmaxf(t2, t3));
+      }
+      if constexpr (NB == 1) tmax[1] = tmax[0];
+      across_groups<true>(tmax[0], tmax[1]);
+
+      // raise the stabiliser only when the half-tile maximum passes it by tau
+      bool raise = false;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) raise = raise || tmax[b] + S.msub[b] > S.m_run[b] + kTau;
+      if (__ballot(raise) != 0ull) {
+        if (ht == 1) {  // the first half's P~ belong to the old stabiliser
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int w = 4; w < 8; ++w) pk[b][w] = 0;
+          pv(kOne);
+          if constexpr (two) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) pk[b][j] = residual_fp8x4(p1[j][b][0], p1[j][b][1], p1[j][b][2],
+                                                                    p1[j][b][3], pk[b][j], 0);
+            pv(kOne - kLoShift);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              pk[b][w] = 0;
+              if constexpr (two) p1[w][b] = v4f{0.f, 0.f, 0.f, 0.f};  // no residual left either
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float m_new = fmaxf(S.m_run[b], tmax[b] + S.msub[b]);
+          const float alpha = S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
+          S.l_part[b][0] *= alpha;
+          S.l_part[b][1] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) S.o[db][b] *= alpha;
+          const float shift = m_new == -INFINITY ? 0.f : m_new - S.msub[b];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[j][b] -= shift;
+          S.m_run[b] = m_new;
+          S.msub[b] = m_new == -INFINITY ? 0.f : m_new;
+        }
+      }
+
+      // P~ = 2^z, l += P~ / s_v, P~ to FP8 (B operand of P V: byte 4 sb + i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sb = 4 * ht + j;
+        const v4f iv = *reinterpret_cast<const v4f*>(tg + kFacIv + 4 * sb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[j][b][i] = __builtin_amdgcn_exp2f(s[j][b][i]);
+            S.l_part[b][i & 1] = fmaf(s[j][b][i], iv[i], S.l_part[b][i & 1]);
+          }
+          pk[b][sb] = cvt_fp8x4_over(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3], 0);
+          if constexpr (two) {
+            if (ht == 0) p1[j][b] = s[j][b];
+          }
+        }
+      }
+      if constexpr (two) {
+        if (ht == 1) {
+          // both halves' first-term codes are in pk: multiply them, then the
+          // residual codes of both halves
+          pv(kOne);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              pk[b][j] = residual_fp8x4(p1[j][b][0], p1[j][b][1], p1[j][b][2], p1[j][b][3], pk[b][j], 0);
+              pk[b][4 + j] = residual_fp8x4(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3], pk[b][4 + j], 0);
+            }
+          pv(kOne - kLoShift);
+        }
+      }
     }
+    if constexpr (!two) pv(kOne);
   };
 
   auto step = [&](auto& S, uint8_t* cur, uint8_t* nxt, float* fcur, float* fnxt, int st)
@@ -700,21 +671,26 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     wait_lgkm0();
     bare_barrier();  // tile st and its tables are visible; every wave is done with `nxt`
     const bool more = st + 1 < n_steps;
-    if (more) issue(nxt, st + 1);
     if (fac_wave && more) {
       const float ks = m_ks, vs = m_vs;
       const int kb = m_kb;
       if (st + 2 < n_steps) meta_load(st + 2, m_ks, m_vs, m_kb);
       fac_write(fnxt, ks, vs, kb);
     }
-    if (!wave_active || !has_tile(st, kh)) return;
     const float* tbl = fcur + kh * kFacWords;
     const uint8_t* buf = cur + kh * T::bytes;
     bool vis[2], fast[2], hist[2];
     classify(tbl, 0, vis[0], fast[0], hist[0]);
     classify(tbl, 1, vis[1], fast[1], hist[1]);
-    if (!vis[0] && !vis[1]) return;
-    tile(S, buf, tbl, vis[0] && vis[1] && fast[0] && fast[1], hist);
+    if (!wave_active || !has_tile(st, kh) || (!vis[0] && !vis[1])) {
+      if (more) issue(nxt, st + 1);
+      return;
+    }
+    // past the last step the loads have no tile of their own: they reload a
+    // valid one into the buffer nobody reads, so every wave issues the same
+    // loads (the compiler then needs no waits of its own)
+    tile(S, buf, tbl, vis[0] && vis[1] && fast[0] && fast[1], hist,
+         [&](int j) __attribute__((always_inline)) { issue_j(nxt, st + 1, j); });
   };
 
   // Merge the two key halves through LDS (the stage buffers are free then)
@@ -791,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     }
   };
 
-  if (!precise) {
+  if constexpr (!TWO) {
     BlkState<NDB, 2> S;
     prep_q(S, 0);
     if (fac_wave) fac_write(fac0, m2_ks, m2_vs, m2_kb);
@@ -871,12 +847,6 @@ hipError_t fp8_impl(const RingView& r, const AttnCall& c, int splits, hipStream_
   a.scale_log2 = sigma * kLog2e;
   const float bias = c.same_block ? 0.f : c.cache_bias;
   a.bias_log2 = bias * kLog2e;
-  const double u1 = std::exp(-std::fabs(static_cast<double>(bias))), u2 = u1 * u1;
-  a.ws1 = bias < 0.f ? 1.f : static_cast<float>(u1);
-  a.we1 = bias < 0.f ? static_cast<float>(u1) : 1.f;
-  a.ws2 = bias < 0.f ? 1.f : static_cast<float>(u2);
-  a.we2 = bias < 0.f ? static_cast<float>(u2) : 1.f;
-  a.precision = c.precision;
   a.out = c.out;
   a.lse = c.lse;
   a.n_qt = (c.n_q + kQT - 1) / kQT;
@@ -893,10 +863,12 @@ hipError_t fp8_impl(const RingView& r, const AttnCall& c, int splits, hipStream_
   const int total = a.n_qt * r.H * splits;
   a.remap = (total % 8 == 0) ? 1 : 0;
   a.n_items = total;
-  if (a.q_block_ids || a.same_block)
-    hipLaunchKernelGGL((attn_fp8_kernel<D, true>), dim3(total), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_fp8_kernel<D, false>), dim3(total), dim3(kThreads), 0, s, a);
+  const bool gen = a.q_block_ids || a.same_block;
+  const bool two = c.precision == 1;
+  if (gen && two) hipLaunchKernelGGL((attn_fp8_kernel<D, true, true>), dim3(total), dim3(kThreads), 0, s, a);
+  else if (gen) hipLaunchKernelGGL((attn_fp8_kernel<D, true, false>), dim3(total), dim3(kThreads), 0, s, a);
+  else if (two) hipLaunchKernelGGL((attn_fp8_kernel<D, false, true>), dim3(total), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((attn_fp8_kernel<D, false, false>), dim3(total), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int rows = c.n_q * r.H;

@@ -34,7 +34,8 @@
 // The layout the Python binding mirrors.
 static_assert(offsetof(rc_ring, n_anchor) == 24 && offsetof(rc_ring, n_memory) == 28, "rc_ring layout");
 static_assert(offsetof(rc_ring, k) == 32 && offsetof(rc_ring, head) == 80, "rc_ring layout");
-static_assert(offsetof(rc_ring, n_mem) == 100 && sizeof(rc_ring) == 104, "rc_ring layout");
+static_assert(offsetof(rc_ring, n_mem) == 100 && offsetof(rc_ring, max_block) == 104, "rc_ring layout");
+static_assert(sizeof(rc_ring) == 112, "rc_ring layout");
 
 namespace {
 
@@ -98,7 +99,7 @@ int32_t ring_end(const rc_ring* r) { return r->n_slots - r->n_memory; }
 rc_status check_state(const rc_ring* r) {
   const int E = ring_end(r);
   if (r->head < 0 || r->head >= E || r->n_hist < 0 || r->n_cur < 0 || r->n_hist + r->n_cur > E ||
-      r->n_mem < 0 || r->n_mem > r->n_memory)
+      r->n_mem < 0 || r->n_mem > r->n_memory || r->max_block < -1)
     return fail(RC_ERR_STATE, "ring host state is corrupt (head %d, n_hist %d, n_cur %d, n_mem %d, E %d)", r->head,
                 r->n_hist, r->n_cur, r->n_mem, E);
   return RC_OK;
@@ -163,7 +164,36 @@ rc_status do_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_n
   r->n_cur = n_new;
   r->cur_pos0 = pos0;
   r->cur_block = block_id;
+  r->max_block = std::max(r->max_block, block_id);
   return ok();
+}
+
+// Operand precision of one FP8 attention call (RC_PRECISION_AUTO resolved;
+// see rc_set_attention_precision in rc.h).  The effective number of keys of a
+// query that sees x slots of its own block (weight 1) and n - x earlier ones
+// (weight w = exp(bias)) is f(x) = (x + (n - x) w)^2 / (x + (n - x) w^2); f
+// falls to its minimum 4 n w / (1 + w)^2 at x* = n w / (1 + w) and rises
+// after, so over the splits x >= x_lo the bound is f(max(x*, x_lo)).
+constexpr double kFastMinKeys = 2048.0;
+
+int attention_precision(const rc_ring* r, int mode, const int32_t* q_block, int32_t n_q, int32_t q_block0,
+                        int32_t q_block_len, int32_t mask, float cache_bias) {
+  if (mode != RC_PRECISION_AUTO) return mode;
+  if (q_block || mask != RC_MASK_BLOCK_CAUSAL) return RC_PRECISION_TWO_TERM;
+  if (q_block0 + (n_q - 1) / q_block_len != q_block0) return RC_PRECISION_TWO_TERM;
+  if (r->max_block < 0 || q_block0 < r->max_block) return RC_PRECISION_TWO_TERM;
+  const double n = static_cast<double>(r->n_hist) + r->n_cur + r->n_mem;
+  const double x_lo = (q_block0 == r->cur_block && r->n_cur > 0) ? r->n_cur : 0.0;
+  if (q_block0 > r->max_block || n <= 0.0) {  // no slot is in the queries' block
+    const double w = std::exp(static_cast<double>(cache_bias));
+    return n > 0.0 && std::isfinite(w) && w > 0.0 && n >= kFastMinKeys ? RC_PRECISION_ONE_TERM
+                                                                       : RC_PRECISION_TWO_TERM;
+  }
+  const double w = std::exp(static_cast<double>(cache_bias));
+  if (!std::isfinite(w)) return RC_PRECISION_TWO_TERM;
+  const double x = std::min(n, std::max(n * w / (1.0 + w), x_lo));
+  const double u = x + (n - x) * w, v = x + (n - x) * w * w;
+  return v > 0.0 && u * u >= kFastMinKeys * v ? RC_PRECISION_ONE_TERM : RC_PRECISION_TWO_TERM;
 }
 
 }  // namespace
@@ -205,6 +235,7 @@ rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
   r->cur_pos0 = 0;
   r->cur_block = 0;
   r->n_mem = 0;
+  r->max_block = -1;
   return ok();
 }
 
@@ -279,6 +310,7 @@ rc_status rc_qkv_project_write(rc_ring* r, const void* x, int32_t n, int32_t C, 
   r->n_cur = n;
   r->cur_pos0 = pos0;
   r->cur_block = block_id;
+  r->max_block = std::max(r->max_block, block_id);
   return ok();
 }
 
@@ -333,7 +365,9 @@ rc_status rc_chunk_attention_ex(const rc_ring* r, const void* q, int32_t n_q, in
                  workspace_bytes};
   c.q_block_ids = q_block;
   c.same_block = mask == RC_MASK_SAME_BLOCK;
-  c.precision = g_precision.load();
+  c.precision = r->kv_dtype == RC_FP8_E4M3 ? attention_precision(r, g_precision.load(), q_block, n_q, q_block0,
+                                                                   c.q_block_len, mask, cache_bias)
+                                            : RC_PRECISION_AUTO;
   hipError_t e = rc::launch_chunk_attention(view(r), c, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk attention");
   return ok();

@@ -43,7 +43,7 @@ struct AttnCall {
   size_t workspace_bytes;
   const int32_t* q_block_ids = nullptr;  // [n_q] or null (q_block0 + i / q_block_len)
   int same_block = 0;                    // 1: visible iff slot block == query block
-  int precision = 0;                     // FP8 rings: 0 by key count, 1 two-term Q and P, 2 one-term
+  int precision = 0;                     // FP8 rings: 1 two-term Q and P, 2 one-term (resolved on the host)
 };
 
 // Whether an attention kernel is built for this KV format and head size.

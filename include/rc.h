@@ -88,6 +88,8 @@ typedef enum {
  *   n_cur      tokens of the current, not yet committed, chunk (0 = none)
  *   cur_pos0, cur_block   position of the current chunk's first token, its block
  *   n_mem      occupied memory slots; they are always slots E .. E + n_mem - 1
+ *   max_block  largest block id written since rc_ring_init (-1: none); the FP8
+ *              attention's automatic operand precision reads it
  */
 typedef struct rc_ring {
   int32_t n_slots;     /* N >= 1 */
@@ -104,7 +106,7 @@ typedef struct rc_ring {
   float* v_scale;
   int32_t* slot_pos;
   int32_t* slot_block;
-  int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem;
+  int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem, max_block;
 } rc_ring;
 
 /* Leading dimension of the transposed V buffer: N rounded up to 128 (a whole
@@ -219,16 +221,20 @@ rc_status rc_chunk_attention_ex(const rc_ring* ring, const void* q, int32_t n_q,
  * square root of the effective number of keys a query sees (Runway
  * Characters, abstract: FP8 KV cache; the rest of the attention's arithmetic
  * is the block-causal softmax of rc_chunk_attention).
- *   RC_PRECISION_AUTO      (0, default) per workgroup of 128 queries of one
- *                          head: one FP8 term for Q and for P when all its
- *                          queries lie in one block b and
- *                          (n_b + n_<b w)^2 / (n_b + n_<b w^2) >= 2048, where
- *                          n_b / n_<b count the slots of block b / of earlier
- *                          blocks and w = exp(cache_bias) (for the same-block
- *                          mask n_<b = 0); two terms (the codes of the residual
+ *   RC_PRECISION_AUTO      (0, default) one FP8 term for Q and for P when the
+ *                          call's queries all lie in one block b >= max_block
+ *                          (so every occupied slot is visible), the mask is
+ *                          block-causal, and a lower bound of the effective
+ *                          number of keys (n_b + n_<b w)^2 / (n_b + n_<b w^2)
+ *                          reaches 2048, where w = exp(cache_bias), the
+ *                          n_hist + n_cur + n_mem occupied slots split into
+ *                          n_b slots of block b (at least n_cur when b is the
+ *                          current chunk's block) and n_<b earlier ones, and
+ *                          the bound is the minimum over the splits the ring
+ *                          state allows; two terms (the codes of the residual
  *                          at 1/16 of the scale added) otherwise
- *   RC_PRECISION_TWO_TERM  (1) two terms everywhere
- *   RC_PRECISION_ONE_TERM  (2) one term everywhere
+ *   RC_PRECISION_TWO_TERM  (1) two terms for every call
+ *   RC_PRECISION_ONE_TERM  (2) one term for every call
  * RC_ERR_ARG for any other mode.  Calls already enqueued are not affected.
  */
 typedef enum { RC_PRECISION_AUTO = 0, RC_PRECISION_TWO_TERM = 1, RC_PRECISION_ONE_TERM = 2 } rc_precision;

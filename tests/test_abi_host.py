@@ -43,7 +43,7 @@ def test_struct_layout_matches_c():
     assert RcRing.n_anchor.offset == 24 and RcRing.n_memory.offset == 28
     assert RcRing.k.offset == 32 and RcRing.slot_block.offset == 72
     assert RcRing.head.offset == 80 and RcRing.cur_block.offset == 96 and RcRing.n_mem.offset == 100
-    assert ctypes.sizeof(RcRing) == 104
+    assert RcRing.max_block.offset == 104 and ctypes.sizeof(RcRing) == 112
 
 
 FAKE = 1 << 20  # aligned placeholder address; never dereferenced by the checks below
