@@ -29,6 +29,7 @@ class RcRing(ctypes.Structure):
         ("slot_pos", c_void_p), ("slot_block", c_void_p),
         ("head", c_int32), ("n_hist", c_int32), ("n_cur", c_int32), ("cur_pos0", c_int32),
         ("cur_block", c_int32), ("n_mem", c_int32), ("max_block", c_int32),
+        ("pos_lo", c_int32), ("pos_hi", c_int32),
     ]
 
 

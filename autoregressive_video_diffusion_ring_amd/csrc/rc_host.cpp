@@ -35,7 +35,8 @@
 static_assert(offsetof(rc_ring, n_anchor) == 24 && offsetof(rc_ring, n_memory) == 28, "rc_ring layout");
 static_assert(offsetof(rc_ring, k) == 32 && offsetof(rc_ring, head) == 80, "rc_ring layout");
 static_assert(offsetof(rc_ring, n_mem) == 100 && offsetof(rc_ring, max_block) == 104, "rc_ring layout");
-static_assert(sizeof(rc_ring) == 112, "rc_ring layout");
+static_assert(offsetof(rc_ring, pos_lo) == 108 && offsetof(rc_ring, pos_hi) == 112, "rc_ring layout");
+static_assert(sizeof(rc_ring) == 120, "rc_ring layout");
 
 namespace {
 
@@ -155,6 +156,13 @@ rc_status check_write(const rc_ring* r, const void* k_new, const void* v_new, in
   return RC_OK;
 }
 
+// Widen the bound of cached positions by a write of n tokens from pos0 (the
+// caller has checked pos0 + n - 1 <= INT32_MAX).
+void note_positions(rc_ring* r, int32_t pos0, int32_t n) {
+  r->pos_lo = std::min(r->pos_lo, pos0);
+  r->pos_hi = std::max(r->pos_hi, pos0 + (n - 1));
+}
+
 // Launch the write and update the host state.
 rc_status do_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_new, int32_t pos0, int32_t block_id,
                    hipStream_t stream) {
@@ -165,6 +173,7 @@ rc_status do_write(rc_ring* r, const void* k_new, const void* v_new, int32_t n_n
   r->cur_pos0 = pos0;
   r->cur_block = block_id;
   r->max_block = std::max(r->max_block, block_id);
+  note_positions(r, pos0, n_new);
   return ok();
 }
 
@@ -236,6 +245,8 @@ rc_status rc_ring_init(rc_ring* r, int32_t first_slot, void* stream) {
   r->cur_block = 0;
   r->n_mem = 0;
   r->max_block = -1;
+  r->pos_lo = INT32_MAX;
+  r->pos_hi = INT32_MIN;
   return ok();
 }
 
@@ -311,6 +322,7 @@ rc_status rc_qkv_project_write(rc_ring* r, const void* x, int32_t n, int32_t C, 
   r->cur_pos0 = pos0;
   r->cur_block = block_id;
   r->max_block = std::max(r->max_block, block_id);
+  note_positions(r, pos0, n);
   return ok();
 }
 
@@ -319,12 +331,19 @@ rc_status rc_cache_rerotate(rc_ring* r, int32_t delta, void* stream) {
   if (st != RC_OK) return st;
   if ((st = check_state(r)) != RC_OK) return st;
   if (!(r->rope_base > 0.f)) return fail(RC_ERR_ARG, "rerotate needs a ring with RoPE (rope_base > 0)");
-  if (r->n_cur > 0 && (static_cast<long long>(r->cur_pos0) + delta < INT32_MIN ||
-                       static_cast<long long>(r->cur_pos0) + delta + r->n_cur > INT32_MAX))
-    return fail(RC_ERR_ARG, "positions overflow int32");
+  // every cached position lies in pos_lo .. pos_hi (a superset once slots
+  // are evicted), whether or not a chunk is current
+  const bool written = r->pos_lo <= r->pos_hi;
+  if (written && (static_cast<long long>(r->pos_lo) + delta < INT32_MIN ||
+                  static_cast<long long>(r->pos_hi) + delta > INT32_MAX))
+    return fail(RC_ERR_ARG, "delta %d takes cached positions %d..%d outside int32", delta, r->pos_lo, r->pos_hi);
   hipError_t e = rc::launch_rerotate(view(r), delta, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "rerotate");
   if (r->n_cur > 0) r->cur_pos0 += delta;
+  if (written) {
+    r->pos_lo += delta;
+    r->pos_hi += delta;
+  }
   return ok();
 }
 

@@ -90,6 +90,10 @@ typedef enum {
  *   n_mem      occupied memory slots; they are always slots E .. E + n_mem - 1
  *   max_block  largest block id written since rc_ring_init (-1: none); the FP8
  *              attention's automatic operand precision reads it
+ *   pos_lo, pos_hi   least and greatest token position written since
+ *              rc_ring_init, both moved by every re-rotation (pos_lo > pos_hi:
+ *              nothing written); a bound of every cached slot's position,
+ *              which rc_cache_rerotate keeps inside int32
  */
 typedef struct rc_ring {
   int32_t n_slots;     /* N >= 1 */
@@ -106,7 +110,7 @@ typedef struct rc_ring {
   float* v_scale;
   int32_t* slot_pos;
   int32_t* slot_block;
-  int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem, max_block;
+  int32_t head, n_hist, n_cur, cur_pos0, cur_block, n_mem, max_block, pos_lo, pos_hi;
 } rc_ring;
 
 /* Leading dimension of the transposed V buffer: N rounded up to 128 (a whole
@@ -122,10 +126,14 @@ rc_status rc_ring_sizes(int32_t n_slots, int32_t n_heads, int32_t head_dim, int3
                         size_t out[6]);
 
 /*
+ * Start an empty ring cache (Runway Characters, abstract: the KV cache is a
+ * ring that every chunk writes once; an empty ring has no visible slot).
  * Validate the geometry and pointers, zero K, V and the scales, set every
  * slot_block to -1 and slot_pos to 0 (asynchronously on `stream`), and set the
  * host state: head = first_slot (0 <= first_slot < N - n_memory; 0 when
- * n_anchor > 0), n_hist = n_cur = n_mem = 0.
+ * n_anchor > 0), n_hist = n_cur = n_mem = 0, max_block = -1, pos_lo =
+ * INT32_MAX, pos_hi = INT32_MIN.  RC_ERR_ARG for
+ * a null ring or pointer, a bad geometry or first_slot out of range.
  */
 rc_status rc_ring_init(rc_ring* ring, int32_t first_slot, void* stream);
 
@@ -155,12 +163,17 @@ rc_status rc_cache_write(rc_ring* ring, const void* k_new, const void* v_new, in
  * chunk) has its key rotated by delta: FP8 codes are dequantised, rotated,
  * and quantised again with a fresh absmax scale.  slot_pos += delta for those
  * slots, and cur_pos0 += delta when a chunk is current.  V is untouched.
- * Requires rope_base > 0.
+ * Requires rope_base > 0.  RC_ERR_ARG when delta would take a cached
+ * position (any position in pos_lo .. pos_hi) outside int32.
  */
 rc_status rc_cache_rerotate(rc_ring* ring, int32_t delta, void* stream);
 
 /*
- * Block-causal chunk attention of n_q queries over every cached slot.
+ * Block-causal chunk attention of n_q queries over every cached slot: the
+ * chunk's queries attend over the whole ring on every call (Runway
+ * Characters, abstract), earlier blocks' logits take the scalar cache bias
+ * (video-conductor, "Plastic Windows"), and the mask is full inside a block
+ * and backward-only across blocks (StreamLTX project page, Training).
  *   q            device [n_q][H][d], bfloat16 (float32 for an RC_F32 ring),
  *                not yet rotated; query i has position q_pos0 + i and block
  *                q_block0 + i / q_block_len
@@ -244,9 +257,12 @@ rc_status rc_set_attention_precision(int32_t mode);
 size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
 
 /*
- * Commit the current chunk as history (host only, nothing is enqueued):
- * head moves n slots on (wrapping from E to n_anchor), n_hist =
- * min(n_hist + n, E), n_cur = 0.  Requires n == n_cur > 0.
+ * Commit the current chunk as history once its last denoising pass is done
+ * (Runway Characters, abstract: each chunk's keys and values are written
+ * once and then serve every later chunk from the ring).  Host only, nothing
+ * is enqueued: head moves n slots on (wrapping from E to n_anchor), n_hist =
+ * min(n_hist + n, E), n_cur = 0.  Requires n == n_cur > 0 (RC_ERR_STATE
+ * otherwise, RC_ERR_ARG for a null ring).
  */
 rc_status rc_ring_advance(rc_ring* ring, int32_t n);
 

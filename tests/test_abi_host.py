@@ -38,12 +38,13 @@ def test_library_exports_every_header_symbol():
 
 
 def test_struct_layout_matches_c():
-    # int32 x 4, float, int32 x 3, then six pointers at 8-byte alignment, then 6 int32
+    # int32 x 4, float, int32 x 3, then six pointers at 8-byte alignment, then 9 int32
     # (the library checks the same offsets with static_asserts)
     assert RcRing.n_anchor.offset == 24 and RcRing.n_memory.offset == 28
     assert RcRing.k.offset == 32 and RcRing.slot_block.offset == 72
     assert RcRing.head.offset == 80 and RcRing.cur_block.offset == 96 and RcRing.n_mem.offset == 100
-    assert RcRing.max_block.offset == 104 and ctypes.sizeof(RcRing) == 112
+    assert RcRing.max_block.offset == 104 and RcRing.pos_lo.offset == 108 and RcRing.pos_hi.offset == 112
+    assert ctypes.sizeof(RcRing) == 120
 
 
 FAKE = 1 << 20  # aligned placeholder address; never dereferenced by the checks below
@@ -294,3 +295,27 @@ def test_attention_ex_checks():
     assert call(mask=-1) == RC_ERR_ARG
     assert call(bl=0) == RC_ERR_ARG            # no block array and no block length
     assert call(qb=FAKE + 2, bl=0) == RC_ERR_ARG   # misaligned block array
+
+
+def test_rerotate_rejects_position_overflow_with_no_current_chunk():
+    """A reset right after rc_ring_advance (n_cur == 0) must still keep every
+    cached position inside int32: the bound is the ring's pos_lo .. pos_hi,
+    not the current chunk.  Rejections enqueue nothing and change nothing;
+    an accepted delta gets as far as the launch (which has no GPU here)."""
+    L = lib()
+    r = fake_ring(100, head=40, n_hist=40, n_cur=0)
+    r.pos_lo, r.pos_hi = 2_000_000_000, 2_100_000_000
+    before = state(r) + (r.pos_lo, r.pos_hi)
+    for delta in (100_000_000, 47_483_648, 2**31 - 1):
+        assert L.rc_cache_rerotate(ctypes.byref(r), delta, None) == RC_ERR_ARG, delta
+        assert "outside int32" in L.rc_last_error().decode()
+        assert state(r) + (r.pos_lo, r.pos_hi) == before
+    r.pos_lo, r.pos_hi = -2_100_000_000, -2_000_000_000
+    assert L.rc_cache_rerotate(ctypes.byref(r), -47_483_649, None) == RC_ERR_ARG
+    # the largest delta that still fits passes the check (and fails only at the launch)
+    r.pos_lo, r.pos_hi = 2_000_000_000, 2_100_000_000
+    got = L.rc_cache_rerotate(ctypes.byref(r), 2**31 - 1 - 2_100_000_000, None)
+    assert got != RC_ERR_ARG, L.rc_last_error()
+    # nothing written (pos_lo > pos_hi): any delta passes the check
+    r.pos_lo, r.pos_hi = 2**31 - 1, -2**31
+    assert L.rc_cache_rerotate(ctypes.byref(r), 2**31 - 1, None) != RC_ERR_ARG
