@@ -99,10 +99,15 @@ int32_t ring_end(const rc_ring* r) { return r->n_slots - r->n_memory; }
 
 rc_status check_state(const rc_ring* r) {
   const int E = ring_end(r);
-  if (r->head < 0 || r->head >= E || r->n_hist < 0 || r->n_cur < 0 || r->n_hist + r->n_cur > E ||
+  if (r->head < 0 || r->head >= E || r->n_hist < 0 || r->n_cur < 0 ||
+      static_cast<long long>(r->n_hist) + r->n_cur > E ||
       r->n_mem < 0 || r->n_mem > r->n_memory || r->max_block < -1)
     return fail(RC_ERR_STATE, "ring host state is corrupt (head %d, n_hist %d, n_cur %d, n_mem %d, E %d)", r->head,
                 r->n_hist, r->n_cur, r->n_mem, E);
+  // the current chunk's positions lie inside the bound of cached positions
+  if (r->n_cur > 0 && (r->cur_pos0 < r->pos_lo || static_cast<long long>(r->cur_pos0) + r->n_cur - 1 > r->pos_hi))
+    return fail(RC_ERR_STATE, "ring host state is corrupt (chunk positions %d + %d outside %d..%d)", r->cur_pos0,
+                r->n_cur, r->pos_lo, r->pos_hi);
   return RC_OK;
 }
 
@@ -375,6 +380,10 @@ rc_status rc_chunk_attention_ex(const rc_ring* r, const void* q, int32_t n_q, in
   if (q_block && (reinterpret_cast<uintptr_t>(q_block) & 3u)) return fail(RC_ERR_ARG, "q_block must be 4-byte aligned");
   if (mask != RC_MASK_BLOCK_CAUSAL && mask != RC_MASK_SAME_BLOCK) return fail(RC_ERR_ARG, "unknown mask %d", mask);
   if (static_cast<long long>(q_pos0) + n_q - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (!q_block && static_cast<long long>(q_block0) + (n_q - 1) / q_block_len > INT32_MAX)
+    return fail(RC_ERR_ARG, "query blocks overflow int32");
+  // the FP8 operand precision reads the host state
+  if ((st = check_state(r)) != RC_OK) return st;
   if (!std::isfinite(cache_bias) && !(cache_bias < 0.f))
     return fail(RC_ERR_ARG, "cache_bias must be finite or -inf");
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
@@ -420,6 +429,8 @@ rc_status key_mass_impl(const rc_ring* r, const void* q, int32_t n_q, int32_t q_
   if (n_q < 1) return fail(RC_ERR_ARG, "n_q must be >= 1 (got %d)", n_q);
   if (q_block_len < 1) return fail(RC_ERR_ARG, "q_block_len must be >= 1 (got %d)", q_block_len);
   if (static_cast<long long>(q_pos0) + n_q - 1 > INT32_MAX) return fail(RC_ERR_ARG, "positions overflow int32");
+  if (static_cast<long long>(q_block0) + (n_q - 1) / q_block_len > INT32_MAX)
+    return fail(RC_ERR_ARG, "query blocks overflow int32");
   if (!std::isfinite(cache_bias) && !(cache_bias < 0.f))
     return fail(RC_ERR_ARG, "cache_bias must be finite or -inf");
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)

@@ -58,6 +58,8 @@ def fake_ring(N, H=2, d=64, kv=RC_FP8_E4M3, head=0, n_hist=0, n_cur=0, n_anchor=
     r.v_ld = lib().rc_ring_v_ld(N)
     r.k = r.v = r.k_scale = r.v_scale = r.slot_pos = r.slot_block = FAKE
     r.head, r.n_hist, r.n_cur = head, n_hist, n_cur
+    r.max_block = -1
+    r.pos_lo, r.pos_hi = 0, 1 << 30  # a bound that covers every position these tests write
     return r
 
 
