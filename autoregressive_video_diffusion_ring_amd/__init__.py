@@ -9,7 +9,7 @@ kernels behind the C ABI.  The entry points keep the C names:
     rc_key_mass, rc_key_mass_slots, rc_key_mass_workspace_bytes,
     rc_cache_write_scored, rc_cache_write_scored_workspace_bytes,
     rc_chunk_attention_ex, rc_qkv_project_write, rc_qkv_workspace_bytes,
-    rc_set_attention_precision
+    rc_set_attention_precision, rc_chunk_attention_noalloc, rc_attention_noalloc_limit
 
 and ``Ring`` owns a ring's device buffers (torch tensors) and its rc_ring
 struct.  See include/rc.h for the meaning of every argument.
@@ -26,6 +26,7 @@ from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, R
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
+    "rc_chunk_attention_noalloc", "rc_attention_noalloc_limit",
     "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_slots", "rc_key_mass_workspace_bytes",
     "rc_cache_write_scored",
     "rc_cache_write_scored_workspace_bytes", "rc_chunk_attention_ex", "RC_MASK_BLOCK_CAUSAL", "RC_MASK_SAME_BLOCK",
@@ -119,6 +120,17 @@ def rc_set_attention_precision(mode: int) -> None:
 
 def rc_attention_workspace_bytes(ring: RcRing, n_q: int) -> int:
     return lib().rc_attention_workspace_bytes(ctypes.byref(ring), n_q)
+
+
+def rc_chunk_attention_noalloc(ring: RcRing, q, n_q: int, q_pos0: int, q_block0: int, q_block_len: int,
+                               cache_bias: float, softmax_scale: float, out, lse=None, stream=None) -> None:
+    check(lib().rc_chunk_attention_noalloc(ctypes.byref(ring), _ptr(q), n_q, q_pos0, q_block0, q_block_len,
+                                           float(cache_bias), float(softmax_scale), _ptr(out), _ptr(lse),
+                                           _stream(stream)))
+
+
+def rc_attention_noalloc_limit() -> int:
+    return lib().rc_attention_noalloc_limit()
 
 
 def rc_ring_advance(ring: RcRing, n: int) -> None:

@@ -54,6 +54,9 @@ SIGNATURES = {
                                         c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "rc_set_attention_precision": (c_int32, [c_int32]),
     "rc_attention_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
+    "rc_chunk_attention_noalloc": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
+                                             c_float, c_void_p, c_void_p, c_void_p]),
+    "rc_attention_noalloc_limit": (c_size_t, []),
     "rc_qkv_project_write": (c_int32, [POINTER(RcRing), c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32,
                                        c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "rc_qkv_workspace_bytes": (c_size_t, [c_int32, c_int32]),

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librc.so")
 
-SOURCES = ["rc_host.cpp", "cache_write.hip", "chunk_attn.hip", "attn_fp8.hip", "memory.hip", "qkv_write.hip"]
+SOURCES = ["rc_host.cpp", "cache_write.hip", "chunk_attn.hip", "attn_fp8.hip", "memory.hip", "qkv_write.hip",
+           "noalloc.hip"]
 
 # Packed fp32 instructions are disabled for device code: they are generated
 # only from ordinary float code and are not needed on any path here.

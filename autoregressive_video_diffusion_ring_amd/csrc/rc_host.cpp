@@ -54,6 +54,20 @@ rc_status fail(rc_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+int rc::host_fail(int st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+namespace {
+
 rc_status ok() {
   g_err.clear();
   return RC_OK;

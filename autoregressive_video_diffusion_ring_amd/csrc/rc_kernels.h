@@ -79,6 +79,9 @@ hipError_t launch_qkv_project_write(const RingView& r, const void* x, int n, int
                                     const float* w_scale, int head, int pos0, int block_id, void* q_out,
                                     void* workspace, hipStream_t s);
 
+// Record a failure for rc_last_error (rc_host.cpp) and return st.
+int host_fail(int st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 hipError_t launch_debug_visibility(const RingView& r, int n_q, int q_block0, int q_block_len,
                                    uint8_t* mask, hipStream_t s);
 

@@ -257,6 +257,24 @@ rc_status rc_set_attention_precision(int32_t mode);
 size_t rc_attention_workspace_bytes(const rc_ring* ring, int32_t n_q);
 
 /*
+ * rc_chunk_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call and the same result, with the key-split partials
+ * kept in a fixed device array of the library (rc_attention_noalloc_limit()
+ * bytes, 16 MiB, held by every GPU the library runs on until the process
+ * ends) instead of a workspace argument.  The call allocates nothing; its
+ * first call on a device looks up that device's array (the device current at
+ * the call).  RC_ERR_ARG when the call would need more than the limit
+ * (rc_attention_workspace_bytes(ring, n_q) bytes), otherwise the checks and
+ * errors of rc_chunk_attention.  Calls that overlap on one GPU share the
+ * array and race: serialise them (one stream per GPU).
+ */
+rc_status rc_chunk_attention_noalloc(const rc_ring* ring, const void* q, int32_t n_q, int32_t q_pos0,
+                                     int32_t q_block0, int32_t q_block_len, float cache_bias, float softmax_scale,
+                                     void* out, float* lse, void* stream);
+size_t rc_attention_noalloc_limit(void);
+
+/*
  * Commit the current chunk as history once its last denoising pass is done
  * (Runway Characters, abstract: each chunk's keys and values are written
  * once and then serve every later chunk from the ring).  Host only, nothing

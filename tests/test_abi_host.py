@@ -321,3 +321,17 @@ def test_rerotate_rejects_position_overflow_with_no_current_chunk():
     # nothing written (pos_lo > pos_hi): any delta passes the check
     r.pos_lo, r.pos_hi = 2**31 - 1, -2**31
     assert L.rc_cache_rerotate(ctypes.byref(r), 2**31 - 1, None) != RC_ERR_ARG
+
+
+def test_noalloc_attention_rejects_calls_beyond_its_scratch():
+    """rc_chunk_attention_noalloc refuses a call whose key-split partials
+    would not fit its fixed array, before anything is enqueued; the limit is
+    the documented 16 MiB."""
+    L = lib()
+    assert L.rc_attention_noalloc_limit() == 16 << 20
+    r = fake_ring(5788, H=64, d=128)
+    need = L.rc_attention_workspace_bytes(ctypes.byref(r), 128)
+    assert need == 4 * 128 * 64 * 129 * 4 > L.rc_attention_noalloc_limit()
+    before = state(r)
+    assert L.rc_chunk_attention_noalloc(ctypes.byref(r), FAKE, 128, 0, 0, 128, 0.0, 0.0, FAKE, FAKE, None) == RC_ERR_ARG
+    assert "no-allocation" in L.rc_last_error().decode() and state(r) == before
