@@ -585,11 +585,16 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       if constexpr (NB == 1) tmax[1] = tmax[0];
       across_groups<true>(tmax[0], tmax[1]);
 
-      // raise the stabiliser only when the half-tile maximum passes it by tau
-      bool raise = false;
+      // raise the stabiliser only when the half-tile maximum passes it by
+      // tau, and only for the queries whose own maximum does: a query's
+      // stabiliser and its rounding never depend on the other queries of its
+      // wave (a raise in the second half-tile multiplies every query's
+      // first-half probabilities into O early, which changes only the order
+      // of one fp32 accumulation for the others)
+      bool own[2] = {false, false};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) raise = raise || tmax[b] + S.msub[b] > S.m_run[b] + kTau;
-      if (__ballot(raise) != 0ull) {
+      for (int b = 0; b < NB; ++b) own[b] = tmax[b] + S.msub[b] > S.m_run[b] + kTau;
+      if (__ballot(own[0] || own[1]) != 0ull) {
         if (ht == 1) {  // the first half's P~ belong to the old stabiliser
 #pragma unroll
           for (int b = 0; b < NB; ++b)
@@ -614,13 +619,14 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const float m_new = fmaxf(S.m_run[b], tmax[b] + S.msub[b]);
-          const float alpha = S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
+          const float m_new = own[b] ? fmaxf(S.m_run[b], tmax[b] + S.msub[b]) : S.m_run[b];
+          const float alpha = !own[b] ? 1.f
+                              : S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
           S.l_part[b][0] *= alpha;
           S.l_part[b][1] *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) S.o[db][b] *= alpha;
-          const float shift = m_new == -INFINITY ? 0.f : m_new - S.msub[b];
+          const float shift = !own[b] || m_new == -INFINITY ? 0.f : m_new - S.msub[b];
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[j][b] -= shift;
           S.m_run[b] = m_new;

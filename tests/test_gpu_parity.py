@@ -75,6 +75,24 @@ def test_tiny_end_to_end():
 
 
 # ------------------------------------------------------------------ writes
+def permute_slots(g, perm):
+    """Move every slot of an FP8 ring (K row, V^T column, scales, position,
+    block) to the physical slot perm[s] was at: slot s gets old slot perm[s]."""
+    H, N, d = g.H, g.N, g.d
+    p = torch.from_numpy(np.asarray(perm)).to(DEV)
+    kb = g.buffers[0].view(H, g.v_ld, d)[:, :N]
+    kb.copy_(kb[:, p].clone())
+    vb = g.buffers[1].view(H, d, g.v_ld)
+    vb[:, :, :N] = vb[:, :, :N][:, :, p].clone()
+    for i in (2, 3):
+        sb = g.buffers[i].view(torch.float32)[:H * g.v_ld].view(H, g.v_ld)[:, :N]
+        sb.copy_(sb[:, p].clone())
+    for i in (4, 5):
+        mb = g.buffers[i].view(torch.int32)[:N]
+        mb.copy_(mb[p].clone())
+    torch.cuda.synchronize()
+
+
 def stream_ring(seed, head0=0, H=40, d=128, N=5788, n_hist=5031, n_new=757):
     """History of n_hist tokens (block 0, positions 0..n_hist-1) committed,
     then the current chunk of n_new tokens (block 1) written."""
@@ -371,19 +389,109 @@ def test_attention_zero_rows_and_scale_spread():
     assert_attention_close(to_np64(out) / 1024.0, ref2 / 1024.0, "fp8")
 
 
-def test_attention_stream_full_size_sampled():
-    banner("attention: streaming layer 757 x 5788 fp8, 40 heads, sampled rows")
+def test_attention_stream_full_size_all_rows():
+    """The streaming layer at its stated size, every one of the 757 rows,
+    against both oracles: the oracle over the GPU's cache codes (the
+    attention alone) and the oracle's own write chain (write + attention end
+    to end)."""
+    banner("attention: streaming layer 757 x 5788 fp8, 40 heads, all rows vs both oracles")
     g, o, rng = stream_ring(WORKLOADS["stream"].seed)
     qt, q = inputs(rng, "fp8", (757, 40, 128))
     lse = torch.empty((40, 757), dtype=torch.float32, device=DEV)
     out = g.attention(qt, 5031, 1, 757, 0.0, lse=lse)
-    rows = np.r_[0:757:9, 750:757]
-    ref, ref_lse = oracle_rows(oracle_from_gpu(g, 10000.0), q, rows, 5031, 1, 757, 0.0)
-    assert_attention_close(out, ref, "fp8", rows=rows)
-    assert np.max(np.abs(to_np64(lse)[:, rows] - ref_lse)) < 5e-2
+    ref, ref_lse = ring_attention(oracle_from_gpu(g, 10000.0), q, 5031, 1, 757, 0.0)
+    err, r = assert_attention_close(out, ref, "fp8")
+    print(f"  vs oracle over GPU codes: max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
+    assert np.max(np.abs(to_np64(lse) - ref_lse)) < 5e-2
+    ref2, _ = ring_attention(o, q, 5031, 1, 757, 0.0)
+    err, r = assert_attention_close(out, ref2, "fp8")
+    print(f"  vs oracle write chain:    max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
     # determinism: the same call twice gives identical bits
     out2 = g.attention(qt, 5031, 1, 757, 0.0)
     assert torch.equal(out, out2)
+
+
+def test_reset_full_size():
+    """Ring wrap + position reset at its stated size: head at slot 5400 (the
+    current chunk wraps), rerotate(-3000), then attention of the chunk's
+    queries at their rebased positions.  Every row against the oracle over
+    the GPU's codes and against the oracle's own write + rerotate chain, and
+    against the same call before the reset."""
+    banner("attention: 757 x 5788 x 40, head 5400, rerotate(-3000), rebased queries, all rows")
+    head0 = (5400 - 5031) % 5788
+    g, o, rng = stream_ring(WORKLOADS["wrap"].seed, head0=head0)
+    assert g.state()[0] == 5400
+    qt, q = inputs(rng, "fp8", (757, 40, 128))
+    before = to_np64(g.attention(qt, 5031, 1, 757, -0.5))
+    g.rerotate(-3000)
+    o.rerotate(-3000)
+    after = to_np64(g.attention(qt, 5031 - 3000, 1, 757, -0.5))
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 5031 - 3000, 1, 757, -0.5)
+    err, r = assert_attention_close(after, ref, "fp8")
+    print(f"  vs oracle over GPU codes: max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
+    ref2, _ = ring_attention(o, q, 5031 - 3000, 1, 757, -0.5)
+    err, r = assert_attention_close(after, ref2, "fp8")
+    print(f"  vs oracle write chain:    max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
+    # RoPE: only relative positions matter, so the reset changes nothing beyond
+    # the keys' FP8 re-quantisation
+    assert_attention_close(after, before, "fp8")
+
+
+def test_slot_permutation_full_size():
+    """Moving slots (with their positions, blocks and scales) to a random
+    permutation of the 5,788 physical slots changes nothing: every row
+    against the oracle of the unpermuted ring, 757 x 5788 x 40."""
+    banner("attention: 757 x 5788 x 40 after a random permutation of the physical slots")
+    g, o, rng = stream_ring(WORKLOADS["stream"].seed + 11)
+    qt, q = inputs(rng, "fp8", (757, 40, 128))
+    ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 5031, 1, 757, -0.5)
+    a = to_np64(g.attention(qt, 5031, 1, 757, -0.5))
+    permute_slots(g, np.random.default_rng(5).permutation(5788))
+    b = to_np64(g.attention(qt, 5031, 1, 757, -0.5))
+    err, r = assert_attention_close(b, ref, "fp8")
+    print(f"  permuted vs oracle: max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
+    assert_attention_close(a, ref, "fp8")
+    assert rel_l2(b, a) < 6e-2
+
+
+def test_attention_query_magnitude_spread():
+    """Queries whose magnitudes spread over 2^-6 .. 2^6 per (token, head),
+    with the softmax scale taken 2^-6 lower so that the largest keep
+    unit-variance logits.  Every row against the oracle; and each query's
+    result depends on its own query only (one FP8 scale per query and head):
+    zeroing the other queries of the call leaves its output bit-identical,
+    in both operand precisions."""
+    from autoregressive_video_diffusion_ring_amd import (RC_PRECISION_AUTO, RC_PRECISION_ONE_TERM,
+                                                         RC_PRECISION_TWO_TERM, rc_set_attention_precision)
+    banner("attention: query magnitudes spread 2^-6 .. 2^6 per (token, head), 256 x 5788 x 8")
+    rng = np.random.default_rng(WORKLOADS["stream"].seed + 29)
+    N, H, d, n_q = 5788, 8, 128, 256
+    g, o = make_pair(N, H, d, "fp8", 10000.0)
+    write_both(g, o, rng, 5031, 0, 0)
+    g.advance(5031)
+    o.advance(5031)
+    write_both(g, o, rng, 757, 5031, 1)
+    u = rng.integers(-6, 7, size=(n_q, H))
+    _, q = inputs(rng, "fp8", (n_q, H, d))
+    q = q * np.exp2(u)[..., None]  # exact in bfloat16 (power-of-two scaling)
+    qt = torch.from_numpy(q.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    assert np.array_equal(to_np64(qt), q)
+    sigma = 2.0 ** -6 / math.sqrt(d)
+    orc = oracle_from_gpu(g, 10000.0)
+    ref, _ = ring_attention(orc, q, 5031, 1, n_q, 0.0, sigma)
+    keep = np.abs(u) < 3
+    q_kept = torch.from_numpy(np.where(keep[..., None], q, 0.0).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    try:
+        for mode in (RC_PRECISION_AUTO, RC_PRECISION_ONE_TERM, RC_PRECISION_TWO_TERM):
+            rc_set_attention_precision(mode)
+            out = g.attention(qt, 5031, 1, n_q, 0.0, softmax_scale=sigma)
+            err, r = assert_attention_close(out, ref, "fp8")
+            print(f"  precision mode {mode}: max-abs {err:.3e}, rel-L2 {r:.3e}", flush=True)
+            out_kept = g.attention(q_kept, 5031, 1, n_q, 0.0, softmax_scale=sigma)
+            same = (out.view(torch.int16) == out_kept.view(torch.int16)).all(dim=2).cpu().numpy()
+            assert same[keep].all(), f"{(~same[keep]).sum()} (query, head) outputs changed"
+    finally:
+        rc_set_attention_precision(RC_PRECISION_AUTO)
 
 
 def test_attention_after_reset_matches_before():
@@ -421,18 +529,7 @@ def test_slot_permutation_invariance():
     g, o, rng = stream_ring(9, H=4, N=640, n_hist=500, n_new=100)
     qt, q = inputs(rng, "fp8", (100, 4, 128))
     a = to_np64(g.attention(qt, 500, 1, 100, -0.5))
-    perm = torch.from_numpy(np.random.default_rng(2).permutation(640)).to(DEV)
-    H, N, d = 4, 640, 128
-    kb = g.buffers[0].view(H, g.v_ld, d)[:, :N]
-    kb.copy_(kb[:, perm].clone())
-    vb = g.buffers[1].view(H, d, g.v_ld)
-    vb[:, :, :N] = vb[:, :, :N][:, :, perm].clone()
-    for i in (2, 3):
-        sb = g.buffers[i].view(torch.float32)[:H * g.v_ld].view(H, g.v_ld)[:, :N]
-        sb.copy_(sb[:, perm].clone())
-    for i in (4, 5):
-        mb = g.buffers[i].view(torch.int32)[:N]
-        mb.copy_(mb[perm].clone())
+    permute_slots(g, np.random.default_rng(2).permutation(640))
     b = to_np64(g.attention(qt, 500, 1, 100, -0.5))
     ref, _ = ring_attention(oracle_from_gpu(g, 10000.0), q, 500, 1, 100, -0.5)
     assert_attention_close(a, ref, "fp8")
