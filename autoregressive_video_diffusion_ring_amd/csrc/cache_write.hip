@@ -337,6 +337,149 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
   }
 }
 
+// FP8 write.  One launch, two kinds of workgroup (uniform per workgroup),
+// neither with LDS or a barrier, so that every wave loads, converts and
+// stores on its own and loads and stores of different waves overlap as in a
+// plain copy:
+//  * K workgroups take (token, head) rows in input order, kKRows per group
+//    of 16 lanes: rotate, quantise and store each row (one d-byte cache row);
+//  * V workgroups take one head and a 128-slot aligned tile of the written
+//    range, 4 consecutive slots x D/16 values per thread; each thread stores,
+//    for each of its values, the 4 slots' codes as one word of the V^T row,
+//    so a wave's store covers 16 consecutive slots of 16 V^T rows and the
+//    workgroup's stores fill whole 128-byte lines (except at the ends of the
+//    written range), merged in the L2 of the one XCD the workgroup runs on.
+// V workgroups of head 0 also write slot_pos and slot_block.
+constexpr int kWThreadsFp8 = 512;
+constexpr int kVTile = 128;     // slots per V workgroup
+constexpr int kVSlots = 4;      // consecutive slots per thread of a V workgroup
+constexpr int kKRows = 2;       // rows per 16-lane group of a K workgroup
+constexpr int kKRowsPerWg = kWThreadsFp8 / kLanesPerRow * kKRows;
+static_assert(kWThreadsFp8 / kLanesPerRow * kVSlots == kVTile, "V tile");
+
+template <int D>
+__global__ __launch_bounds__(kWThreadsFp8) void cache_write_fp8_kernel(WriteArgs a, int k_wgs) {
+  constexpr int EPL = D / kLanesPerRow;  // elements per lane (8 or 4)
+  const int tid = threadIdx.x;
+  const int H = a.r.H, n_new = a.n_new, head = a.head, wrap_tok = a.wrap_tok;
+  const int lo_a = a.lo_a, hi_a = a.hi_a, lo_b = a.lo_b;
+  asm volatile("" ::"s"(H), "s"(n_new), "s"(head), "s"(wrap_tok), "s"(lo_a), "s"(hi_a), "s"(lo_b), "s"(k_wgs));
+  const int piece = tid % kLanesPerRow;
+  const int rg = tid / kLanesPerRow;
+
+  if (static_cast<int>(blockIdx.x) < k_wgs) {
+    // ---- K rows: row index t * H + h (token t, head h), input order
+    const int n_rows = n_new * H;
+    const int row0 = blockIdx.x * kKRowsPerWg + rg * kKRows;
+    Raw<KV_FP8, EPL> rk[kKRows];
+#pragma unroll
+    for (int i = 0; i < kKRows; ++i) {
+#pragma unroll
+      for (int w = 0; w < Raw<KV_FP8, EPL>::words; ++w) rk[i].w[w] = 0u;
+      if (row0 + i < n_rows) load_raw<KV_FP8, EPL>(a.k_new, static_cast<size_t>(row0 + i) * D + piece * EPL, rk[i]);
+    }
+    double rev[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) rev[e] = a.rope.rev[piece * (EPL / 2) + e];
+#pragma unroll
+    for (int i = 0; i < kKRows; ++i) {
+      const int row = row0 + i;
+      const int t = min(row, n_rows - 1) / H, h = min(row, n_rows - 1) % H;
+      float xk[EPL];
+      unpack<KV_FP8, EPL>(rk[i], xk);
+      if (a.use_rope) {
+        const long long pos = static_cast<long long>(a.pos0) + t;
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e) {
+          double r = static_cast<double>(pos) * rev[e];
+          r -= rint(r);
+          const float tt = static_cast<float>(r);
+          const float sn = __builtin_amdgcn_sinf(tt), cs = __builtin_amdgcn_cosf(tt);
+          const float x0 = xk[2 * e], x1 = xk[2 * e + 1];
+          xk[2 * e] = x0 * cs - x1 * sn;
+          xk[2 * e + 1] = x0 * sn + x1 * cs;
+        }
+      }
+      const float ks = row_scale<kLanesPerRow, EPL>(xk);
+      const float krc = scale_rcp(ks);
+      if (row < n_rows) {
+        const int slot = t < hi_a - lo_a ? lo_a + t : lo_b + (t - (hi_a - lo_a));
+        const size_t srow = static_cast<size_t>(h) * a.r.v_ld + slot;
+        // rotated keys: direct product; unrotated keys: exact quotient
+        if (a.use_rope) store_row<KV_FP8, EPL, false>(a.r.k, srow * D + piece * EPL, xk, ks, krc);
+        else store_row<KV_FP8, EPL, true>(a.r.k, srow * D + piece * EPL, xk, ks, krc);
+        if (piece == 0) a.r.k_scale[srow] = ks;
+      }
+    }
+    return;
+  }
+
+  // ---- V tile: head h, slots base .. base + 127 clipped to [lo, hi)
+  const int item = blockIdx.x - k_wgs;
+  const int h = item % H;
+  const int c = item / H;
+  int base, lo, hi;
+  if (c < a.chunks_a) {
+    base = (lo_a / kVTile + c) * kVTile;
+    lo = max(base, lo_a);
+    hi = min(base + kVTile, hi_a);
+  } else {
+    base = (lo_b / kVTile + (c - a.chunks_a)) * kVTile;
+    lo = max(base, lo_b);
+    hi = min(base + kVTile, a.hi_b);
+  }
+  auto token_of = [&](int sl) {
+    int t = sl - head;
+    return t < 0 ? t + wrap_tok : t;
+  };
+  // thread: slots s0 .. s0 + 3, values piece * EPL .. + EPL - 1
+  const int s0 = base + kVSlots * rg;
+  Raw<KV_FP8, EPL> rv[kVSlots];
+#pragma unroll
+  for (int i = 0; i < kVSlots; ++i) {
+#pragma unroll
+    for (int w = 0; w < Raw<KV_FP8, EPL>::words; ++w) rv[i].w[w] = 0u;
+    const int sl = s0 + i;
+    if (sl >= lo && sl < hi)
+      load_raw<KV_FP8, EPL>(a.v_new, (static_cast<size_t>(token_of(sl)) * H + h) * D + piece * EPL, rv[i]);
+  }
+  if (h == 0 && tid < kVTile) {
+    const int sl = base + tid;
+    if (sl >= lo && sl < hi) {
+      a.r.slot_pos[sl] = a.pos0 + token_of(sl);
+      a.r.slot_block[sl] = a.block_id;
+    }
+  }
+  uint32_t code[kVSlots][EPL / 4];
+#pragma unroll
+  for (int i = 0; i < kVSlots; ++i) {
+    float xv[EPL];
+    unpack<KV_FP8, EPL>(rv[i], xv);
+    const float vs = row_scale<kLanesPerRow, EPL>(xv);
+    encode_fp8<EPL, true>(xv, vs, scale_rcp(vs), code[i]);
+    const int sl = s0 + i;
+    if (piece == 0 && sl >= lo && sl < hi) a.r.v_scale[static_cast<size_t>(h) * a.r.v_ld + sl] = vs;
+  }
+  // value j = piece * EPL + e of the 4 slots -> one word of V^T row (h, j)
+  const bool whole = s0 >= lo && s0 + kVSlots <= hi;
+  uint8_t* vrow = static_cast<uint8_t*>(a.r.v) + (static_cast<size_t>(h) * D + piece * EPL) * a.r.v_ld + s0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int sh = 8 * (e % 4);
+    const uint32_t b0 = (code[0][e / 4] >> sh) & 0xFFu, b1 = (code[1][e / 4] >> sh) & 0xFFu;
+    const uint32_t b2 = (code[2][e / 4] >> sh) & 0xFFu, b3 = (code[3][e / 4] >> sh) & 0xFFu;
+    uint8_t* dst = vrow + static_cast<size_t>(e) * a.r.v_ld;
+    if (whole) {
+      *reinterpret_cast<uint32_t*>(dst) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    } else {
+      const uint32_t bytes[4] = {b0, b1, b2, b3};
+#pragma unroll
+      for (int q = 0; q < kVSlots; ++q)
+        if (s0 + q >= lo && s0 + q < hi) dst[q] = static_cast<uint8_t>(bytes[q]);
+    }
+  }
+}
+
 // Delta re-rotation of every occupied row.  A row of K (d elements) is
 // handled by LPR lanes with 16 bytes each; a thread takes kRotRows rows whose
 // loads are all issued before any of the rows' arithmetic.
@@ -448,8 +591,17 @@ hipError_t fill(void* p, size_t bytes, uint32_t value, hipStream_t s) {
 template <int KV, int D>
 hipError_t write_impl(const WriteArgs& a, hipStream_t s) {
   WriteArgs b = a;
-  b.grid = (a.items + 7) / 8 * 8;  // a multiple of 8 for the XCD mapping
-  hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(b.grid), dim3(kThreads), 0, s, b);
+  if constexpr (KV == KV_FP8) {
+    // V tiles of 128 slots, one head each; K rows in blocks of kKRowsPerWg
+    b.chunks_a = (a.hi_a - 1) / kVTile - a.lo_a / kVTile + 1;
+    const int chunks_b = a.hi_b > a.lo_b ? (a.hi_b - 1) / kVTile - a.lo_b / kVTile + 1 : 0;
+    const int v_wgs = (b.chunks_a + chunks_b) * a.r.H;
+    const int k_wgs = (a.n_new * a.r.H + kKRowsPerWg - 1) / kKRowsPerWg;
+    hipLaunchKernelGGL((cache_write_fp8_kernel<D>), dim3(k_wgs + v_wgs), dim3(kWThreadsFp8), 0, s, b, k_wgs);
+  } else {
+    b.grid = (a.items + 7) / 8 * 8;  // a multiple of 8 for the XCD mapping
+    hipLaunchKernelGGL((cache_write_kernel<KV, D>), dim3(b.grid), dim3(kThreads), 0, s, b);
+  }
   return hipGetLastError();
 }
 
