@@ -95,15 +95,16 @@ struct F8Args {
   RopeTable rope;
 };
 
-// LDS geometry of one tile of one key half: K rows [128][D], then V^T rows
-// [D][128 slots].
+// LDS geometry of one tile of one key half: K rows [128][D] in a K stage
+// buffer, V^T rows [D][128 slots] in a V stage buffer.  K and V stages are
+// separate arrays so that the compiler's wait analysis for direct-to-LDS
+// loads (kept per LDS variable) never makes a read of one wait for loads
+// into the other.
 template <int D>
 struct Tile {
   static constexpr int k_cpr = D / 16;  // 16-byte chunks per K row
   static constexpr int k_bytes = kT * D;
-  static constexpr int v_off = k_bytes;
   static constexpr int v_bytes = D * kT;
-  static constexpr int bytes = k_bytes + v_bytes;
   static constexpr int k_instr = k_bytes / 16 / (kQSub * kWave);  // direct loads per wave
   static constexpr int v_instr = v_bytes / 16 / (kQSub * kWave);
   static constexpr int dma_instr = k_instr + v_instr;
@@ -119,9 +120,10 @@ constexpr int kFacWords = 4 * kT + 8;
 
 template <int D>
 struct Lds {
-  static constexpr int stage = kHalves * Tile<D>::bytes;
+  static constexpr int kstage = kHalves * Tile<D>::k_bytes;
+  static constexpr int vstage = kHalves * Tile<D>::v_bytes;
   static constexpr int fac = kHalves * kFacWords;  // words per stage
-  static constexpr int total = 2 * stage + 2 * fac * 4 + 256;
+  static constexpr int total = 2 * kstage + 2 * vstage + 2 * fac * 4 + 512;
   static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -139,8 +141,21 @@ __device__ __forceinline__ int v_swz(int r) { return (r >> 1) & 7; }
 // that output row 4g + i of lane group g is slot 32g + 4sb + i.
 __device__ __forceinline__ int k_perm(int sb, int m) { return 32 * (m >> 2) + 4 * sb + (m & 3); }
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(lds_wave_base), 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw: no stride, no format
+// conversion; loads past the end return zeros).
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+// 16 bytes per lane from the buffer at lane offset off + uniform offset soff
+// straight into LDS (the wave's 64 lanes fill 1024 consecutive bytes).  The
+// buffer form takes a 32-bit lane offset and a scalar offset; the global
+// form of the same load takes a 64-bit vector address per load, whose
+// registers the tile loop cannot spare.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_wave_base), 16, static_cast<int>(off),
+                                           static_cast<int>(soff), 0, 0);
 }
 
 template <int N>
@@ -180,6 +195,13 @@ __device__ __forceinline__ void across_groups(float& x0, float& x1) {
 __device__ __forceinline__ int cvt_fp8x4_over(float a, float b, float c, float d, int old) {
   const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Four floats to four e4m3 codes.  Both halves of the word are written, so
+// the word the first conversion starts from is a's own bits (no register has
+// to be cleared first).
+__device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
+  return cvt_fp8x4_over(a, b, c, d, __float_as_int(a));
 }
 
 // Residual codes of four values whose first-term codes are `hi`:
@@ -244,8 +266,10 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   using T = Tile<D>;
   constexpr int NDB = D / 16;       // d blocks of the output
   constexpr int NG = D / 32;        // lane groups that hold K / Q data (4, or 2 for d 64)
-  __shared__ __attribute__((aligned(16))) uint8_t st0[Lds<D>::stage];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[Lds<D>::stage];
+  __shared__ __attribute__((aligned(16))) uint8_t ks0[Lds<D>::kstage];
+  __shared__ __attribute__((aligned(16))) uint8_t ks1[Lds<D>::kstage];
+  __shared__ __attribute__((aligned(16))) uint8_t vs0[Lds<D>::vstage];
+  __shared__ __attribute__((aligned(16))) uint8_t vs1[Lds<D>::vstage];
   __shared__ __attribute__((aligned(16))) float fac0[Lds<D>::fac];
   __shared__ __attribute__((aligned(16))) float fac1[Lds<D>::fac];
   __shared__ double rev_lds[64];  // RoPE frequencies in revolutions per position
@@ -275,36 +299,49 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   auto has_tile = [&](int li, int half) { return li < n_local && tile_of(li, half) < t_end; };
   const int t_safe = min(t_begin, a.n_tiles - 1);
 
-  // ---- direct-load plan: the lane's byte offsets inside a tile
-  uint32_t k_off[T::k_instr], v_off[T::v_instr];
-#pragma unroll
-  for (int j = 0; j < T::k_instr; ++j) {
-    const int p = (wq * T::k_instr + j) * kWave + lane;
+  // ---- direct-load plan: the lane's byte offsets inside a tile.  Load j of
+  //      a wave covers 1024 bytes: K rows whose swizzle does not depend on j
+  //      (K load j is K load 0 plus 1024 j), and V^T rows 8 (wq v_instr + j)
+  //      + lane / 8, whose swizzle depends on j only through its parity (V
+  //      load j is the offset of its parity plus 8 j rows)
+  uint32_t k_off0, v_off_par[2];
+  {
+    const int p = wq * T::k_instr * kWave + lane;
     const int r = p / T::k_cpr, cp = p % T::k_cpr;
-    k_off[j] = static_cast<uint32_t>(r * D + ((cp ^ k_swz<D>(r)) << 4));
-  }
+    k_off0 = static_cast<uint32_t>(r * D + ((cp ^ k_swz<D>(r)) << 4));
 #pragma unroll
-  for (int j = 0; j < T::v_instr; ++j) {
-    const int p = (wq * T::v_instr + j) * kWave + lane;
-    const int r = p / 8, cp = p % 8;
-    v_off[j] = static_cast<uint32_t>(r * a.v_ld + ((cp ^ v_swz(r)) << 4));
+    for (int par = 0; par < 2; ++par) {
+      const int pv = (wq * T::v_instr + par) * kWave + lane;
+      const int rv = pv / 8, cv = pv % 8;
+      v_off_par[par] = static_cast<uint32_t>((rv - 8 * par) * a.v_ld + ((cv ^ v_swz(rv)) << 4));
+    }
   }
-  // the j-th of this wave's T::dma_instr direct loads of tile li (K blocks first)
-  auto issue_j = [&](uint8_t* stage, int li, int j) __attribute__((always_inline)) {
+  static_assert(T::k_instr * kWave * 16 % (D * 32) == 0, "K swizzle independent of the load index");
+  // this head's K rows [v_ld][D] and V^T rows [D][v_ld] (byte offsets < 2^31)
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(a.k + static_cast<size_t>(h) * a.v_ld * D,
+                                                  static_cast<uint32_t>(a.v_ld) * D);
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(a.v + static_cast<size_t>(h) * D * a.v_ld,
+                                                  static_cast<uint32_t>(a.v_ld) * D);
+  // the j-th of this wave's T::dma_instr direct loads of tile li (K blocks
+  // first) into the K / V stage buffers kst / vst
+  auto issue_j = [&](uint8_t* kst, uint8_t* vst, int li, int j) __attribute__((always_inline)) {
     const int tile = has_tile(li, kh) ? tile_of(li, kh) : t_safe;
-    uint8_t* buf = stage + kh * T::bytes;
     if (j < T::k_instr) {
-      const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + static_cast<size_t>(tile) * kT) * D;
-      dma16(kb + k_off[j], buf + (wq * T::k_instr + j) * 1024);
+      dma16(k_rsrc, k_off0, static_cast<uint32_t>(tile * kT * D + 1024 * j),
+            kst + kh * T::k_bytes + (wq * T::k_instr + j) * 1024);
     } else {
       const int jv = j - T::k_instr;
-      const uint8_t* vb = a.v + static_cast<size_t>(h) * D * a.v_ld + static_cast<size_t>(tile) * kT;
-      dma16(vb + v_off[jv], buf + T::v_off + (wq * T::v_instr + jv) * 1024);
+      dma16(v_rsrc, v_off_par[jv & 1], static_cast<uint32_t>(tile * kT + 8 * jv * a.v_ld),
+            vst + kh * T::v_bytes + (wq * T::v_instr + jv) * 1024);
     }
   };
-  auto issue = [&](uint8_t* stage, int li) __attribute__((always_inline)) {
+  auto issue_k = [&](uint8_t* kst, int li) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < T::dma_instr; ++j) issue_j(stage, li, j);
+    for (int j = 0; j < T::k_instr; ++j) issue_j(kst, nullptr, li, j);
+  };
+  auto issue_v = [&](uint8_t* vst, int li) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = T::k_instr; j < T::dma_instr; ++j) issue_j(nullptr, vst, li, j);
   };
 
   // ---- per-slot metadata for the factor tables.  Wave f of key half 0
@@ -362,10 +399,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   const double rev_lane = wave == 0 && lane < D / 2 ? a.rope.rev[lane] : 0.0;
   float m2_ks = 0.f, m2_vs = 0.f;
   int m2_kb = -1;
-  if (fac_wave) {
-    meta_load(0, m2_ks, m2_vs, m2_kb);
-    meta_load(1, m_ks, m_vs, m_kb);
-  }
+  meta_load(0, m2_ks, m2_vs, m2_kb);  // every wave loads (same load history); half 0 uses them
+  meta_load(1, m_ks, m_vs, m_kb);
   constexpr int kQLoads = 4;  // 16-byte loads per block: d = 32 g .. 32 g + 31 as bf16
   v4u qraw[2][kQLoads];
 #pragma unroll
@@ -374,7 +409,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 #pragma unroll
     for (int r = 0; r < kQLoads; ++r) qraw[b][r] = *reinterpret_cast<const v4u*>(a.q + row + 8 * r);
   }
-  issue(st0, 0);
+  issue_k(ks0, 0);
+  issue_v(vs0, 0);
 
   if (wave == 0) rev_lds[lane] = rev_lane;
 
@@ -445,8 +481,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     k_lane_lo = row * D + (((2 * g) ^ sw) << 4);
     k_lane_hi = row * D + (((2 * g + 1) ^ sw) << 4);
     const int swv = v_swz(n16);
-    v_lane_lo = T::v_off + n16 * kT + (((2 * g) ^ swv) << 4);
-    v_lane_hi = T::v_off + n16 * kT + (((2 * g + 1) ^ swv) << 4);
+    v_lane_lo = n16 * kT + (((2 * g) ^ swv) << 4);
+    v_lane_hi = n16 * kT + (((2 * g + 1) ^ swv) << 4);
   }
 
   int qb_lo = INT32_MAX, qb_hi = INT32_MIN;
@@ -483,220 +519,240 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 
   const int n_steps = n_local;
 
-  // One tile for the query blocks held in S (NB = 2: both, the one-term
-  // path; NB = 1: one block, the two-term path, which runs the tiles once per
-  // block to keep its extra operands in registers), half-tile by half-tile
-  // (slot blocks sb = 4ht .. 4ht + 3):  S'^T = K Q^T + C,
-  // z = A S' (+ bias) - msub, the stabiliser check, P~ = 2^z with
-  // l += P~ / s_v, and after both halves O^T += V^T P^T.  `common` tiles
-  // (both half-tiles visible to every query of the wave with one bias value
-  // each) take the bias per half-tile; the others are masked per score from
-  // the slots' blocks.  If the second half raises the stabiliser, the first
-  // half's probabilities (already FP8, relative to the old stabiliser) are
-  // multiplied into O before O is rescaled.
-  auto tile = [&](auto& S, const uint8_t* buf, const float* tbl, bool common, const bool (&hist)[2], auto&& dma)
-                  __attribute__((always_inline)) {
+  // ---- the pieces of one tile for the query blocks held in S (NB = 2: both,
+  //      one FP8 term; NB = 1: one block, with the residual terms).  kb / vb
+  //      are this key half's K rows and V^T rows of the tile, tbl its factor
+  //      tables.
+  //
+  // O^T += V^T P^T over the tile's 128 slots (psc: the operand scale of pk)
+  auto pv = [&](auto& S, const uint8_t* vb, const auto& pk, int psc) __attribute__((always_inline)) {
+    constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
+    const uint8_t* vl = vb + v_lane_lo;
+    const uint8_t* vh = vb + v_lane_hi;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const v4i lo = *reinterpret_cast<const v4i*>(vl + 16 * db * kT);
+      const v4i hi = *reinterpret_cast<const v4i*>(vh + 16 * db * kT);
+      const v8i vop = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) S.o[db][b] = mfma16(vop, pk[b], S.o[db][b], psc);
+    }
+  };
+  // S'^T = K Q^T + C for half-tile ht (slot blocks sb = 4ht .. 4ht + 3); dma(sb)
+  // may issue one of the next tile's direct loads between matrix instructions
+  auto qk_half = [&](auto& S, const uint8_t* kb, const float* tbl, int ht, auto& s, auto&& dma)
+                     __attribute__((always_inline)) {
     constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
     constexpr bool two = NB == 1;
-    // lane bases; slot block sb and d block db only add constants (the
-    // swizzles depend on the lane alone), so the reads take immediate offsets
-    const uint8_t* kl = buf + k_lane_lo;
-    const uint8_t* kh8 = buf + k_lane_hi;
-    const uint8_t* vl = buf + v_lane_lo;
-    const uint8_t* vh = buf + v_lane_hi;
+    const uint8_t* kl = kb + k_lane_lo;
+    const uint8_t* kh8 = kb + k_lane_hi;
     const float* tg = tbl + 32 * g;
-    v8i pk[NB];
-    // O^T += V^T P^T over the tile's 128 slots (pass 1: the residual codes)
-    auto pv = [&](int psc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const v4i lo = *reinterpret_cast<const v4i*>(vl + 16 * db * kT);
-        const v4i hi = *reinterpret_cast<const v4i*>(vh + 16 * db * kT);
-        const v8i vop = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int b = 0; b < NB; ++b) S.o[db][b] = mfma16(vop, pk[b], S.o[db][b], psc);
+    for (int j = 0; j < 4; ++j) {
+      const int sb = 4 * ht + j;
+      v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (g < NG) {
+        const v4i lo = *reinterpret_cast<const v4i*>(kl + 4 * sb * D);
+        const v4i hi = *reinterpret_cast<const v4i*>(kh8 + 4 * sb * D);
+        kop = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
-    };
-    v4f p1[4][NB];  // fp32 probabilities of the first half (two-term path: residual codes)
+      const v4f cin = *reinterpret_cast<const v4f*>(tg + kFacC + 4 * sb);
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      v4f s[4][NB];
+      for (int b = 0; b < NB; ++b) {
+        s[j][b] = mfma16(kop, S.qf[b], cin, S.qsc[b]);
+        if constexpr (two) s[j][b] = mfma16(kop, S.ql[b], s[j][b], S.qsc_lo[b]);
+      }
+      dma(sb);
+    }
+  };
+  // z = A S' (+ bias) - msub, the masks, the stabiliser check, P~ = 2^z with
+  // l += P~ / s_v, and P~ to FP8 into pk (bytes 4 sb + i of the P V operand).
+  // `common` tiles (both half-tiles visible to every query of the wave with
+  // one bias value each) take the bias per half-tile; the others are masked
+  // per score from the slots' blocks.  If half-tile 1 raises the stabiliser,
+  // half-tile 0's probabilities (already FP8, relative to the old stabiliser)
+  // are multiplied into O (V^T of the tile in vb) before O is rescaled.  The
+  // two-term path ends the tile here: both halves' first-term codes, then
+  // their residual codes, multiplied into O.
+  auto soft_half = [&](auto& S, const float* tbl, const uint8_t* vb, int ht, bool common, bool hist_ht, auto& s,
+                       auto& pk, auto& p1) __attribute__((always_inline)) {
+    constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
+    constexpr bool two = NB == 1;
+    const float* tg = tbl + 32 * g;
+    const float zb = common && hist_ht ? a.bias_log2 : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4f af = *reinterpret_cast<const v4f*>(tg + kFacA + 4 * (4 * ht + j));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float zadd = zb - S.msub[b];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[j][b][i] = fmaf(s[j][b][i], af[i], zadd);
+      }
+    }
+    if (!common) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int sb = 4 * ht + j;
-        v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (g < NG) {
-          const v4i lo = *reinterpret_cast<const v4i*>(kl + 4 * sb * D);
-          const v4i hi = *reinterpret_cast<const v4i*>(kh8 + 4 * sb * D);
-          kop = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        }
-        const v4f cin = *reinterpret_cast<const v4f*>(tg + kFacC + 4 * sb);
+        const v4i kb4 = *reinterpret_cast<const v4i*>(tg + kFacKb + 4 * (4 * ht + j));
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          s[j][b] = mfma16(kop, S.qf[b], cin, S.qsc[b]);
-          if constexpr (two) s[j][b] = mfma16(kop, S.ql[b], s[j][b], S.qsc_lo[b]);
-        }
-        // the next tile's direct loads go out between matrix instructions,
-        // so that their issue (which waits while the load queue is full)
-        // overlaps matrix work
-        if (sb < T::dma_instr) dma(sb);
-      }
-      const float zb = common && hist[ht] ? a.bias_log2 : 0.f;
+          const int qb = S.qb[b];
+          const int lo_qb = same_block ? qb : 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4f af = *reinterpret_cast<const v4f*>(tg + kFacA + 4 * (4 * ht + j));
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float zadd = zb - S.msub[b];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[j][b][i] = fmaf(s[j][b][i], af[i], zadd);
-        }
-      }
-      if (!common) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i kb4 = *reinterpret_cast<const v4i*>(tg + kFacKb + 4 * (4 * ht + j));
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const int qb = S.qb[b];
-            const int lo_qb = same_block ? qb : 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kb = kb4[i];
-              const int cls = !GEN ? visibility_class(kb, qb)
-                                   : (kb < lo_qb || kb > qb) ? kVisNone : (kb < qb ? kVisBias : kVisPlain);
-              const float z = cls == kVisBias ? s[j][b][i] + a.bias_log2 : s[j][b][i];
-              s[j][b][i] = cls == kVisNone ? -INFINITY : z;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int kb = kb4[i];
+            const int cls = !GEN ? visibility_class(kb, qb)
+                                 : (kb < lo_qb || kb > qb) ? kVisNone : (kb < qb ? kVisBias : kVisPlain);
+            const float z = cls == kVisBias ? s[j][b][i] + a.bias_log2 : s[j][b][i];
+            s[j][b][i] = cls == kVisNone ? -INFINITY : z;
           }
         }
       }
-      float tmax[2];
+    }
+    float tmax[2];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float t0 = fmaxf(fmaxf(s[0][b][0], s[0][b][1]), s[0][b][2]);
-        float t1 = fmaxf(fmaxf(s[1][b][0], s[1][b][1]), s[1][b][2]);
-        float t2 = fmaxf(fmaxf(s[2][b][0], s[2][b][1]), s[2][b][2]);
-        float t3 = fmaxf(fmaxf(s[3][b][0], s[3][b][1]), s[3][b][2]);
-        t0 = fmaxf(fmaxf(t0, s[0][b][3]), s[1][b][3]);
-        t2 = fmaxf(fmaxf(t2, s[2][b][3]), s[3][b][3]);
-        tmax[b] = fmaxf(fmaxf(t0, t1), fmaxf(t2, t3));
-      }
-      if constexpr (NB == 1) tmax[1] = tmax[0];
-      across_groups<true>(tmax[0], tmax[1]);
+    for (int b = 0; b < NB; ++b) {
+      float t0 = fmaxf(fmaxf(s[0][b][0], s[0][b][1]), s[0][b][2]);
+      float t1 = fmaxf(fmaxf(s[1][b][0], s[1][b][1]), s[1][b][2]);
+      float t2 = fmaxf(fmaxf(s[2][b][0], s[2][b][1]), s[2][b][2]);
+      float t3 = fmaxf(fmaxf(s[3][b][0], s[3][b][1]), s[3][b][2]);
+      t0 = fmaxf(fmaxf(t0, s[0][b][3]), s[1][b][3]);
+      t2 = fmaxf(fmaxf(t2, s[2][b][3]), s[3][b][3]);
+      tmax[b] = fmaxf(fmaxf(t0, t1), fmaxf(t2, t3));
+    }
+    if constexpr (NB == 1) tmax[1] = tmax[0];
 
-      // raise the stabiliser only when the half-tile maximum passes it by
-      // tau, and only for the queries whose own maximum does: a query's
-      // stabiliser and its rounding never depend on the other queries of its
-      // wave (a raise in the second half-tile multiplies every query's
-      // first-half probabilities into O early, which changes only the order
-      // of one fp32 accumulation for the others)
+    // raise the stabiliser only when the half-tile maximum passes it by
+    // tau, and only for the queries whose own maximum does: a query's
+    // stabiliser and its rounding never depend on the other queries of its
+    // wave (a raise in the second half-tile multiplies every query's
+    // first-half probabilities into O early, which changes only the order
+    // of one fp32 accumulation for the others).  A query's maximum passes
+    // the threshold iff one of its four lanes' maxima does, so the lanes
+    // test their own maxima first and the maxima are combined across the
+    // lane groups only when some lane passes.
+    bool lane_own = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lane_own = lane_own || tmax[b] + S.msub[b] > S.m_run[b] + kTau;
+    if (__ballot(lane_own) != 0ull) {
+      across_groups<true>(tmax[0], tmax[1]);
       bool own[2] = {false, false};
 #pragma unroll
       for (int b = 0; b < NB; ++b) own[b] = tmax[b] + S.msub[b] > S.m_run[b] + kTau;
-      if (__ballot(own[0] || own[1]) != 0ull) {
-        if (ht == 1) {  // the first half's P~ belong to the old stabiliser
+      if (ht == 1) {  // the first half's P~ belong to the old stabiliser
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int w = 4; w < 8; ++w) pk[b][w] = 0;
-          pv(kOne);
-          if constexpr (two) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int b = 0; b < NB; ++b) pk[b][j] = residual_fp8x4(p1[j][b][0], p1[j][b][1], p1[j][b][2],
-                                                                    p1[j][b][3], pk[b][j], 0);
-            pv(kOne - kLoShift);
-          }
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              pk[b][w] = 0;
-              if constexpr (two) p1[w][b] = v4f{0.f, 0.f, 0.f, 0.f};  // no residual left either
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float m_new = own[b] ? fmaxf(S.m_run[b], tmax[b] + S.msub[b]) : S.m_run[b];
-          const float alpha = !own[b] ? 1.f
-                              : S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
-          S.l_part[b][0] *= alpha;
-          S.l_part[b][1] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) S.o[db][b] *= alpha;
-          const float shift = !own[b] || m_new == -INFINITY ? 0.f : m_new - S.msub[b];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s[j][b] -= shift;
-          S.m_run[b] = m_new;
-          S.msub[b] = m_new == -INFINITY ? 0.f : m_new;
-        }
-      }
-
-      // P~ = 2^z, l += P~ / s_v, P~ to FP8 (B operand of P V: byte 4 sb + i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sb = 4 * ht + j;
-        const v4f iv = *reinterpret_cast<const v4f*>(tg + kFacIv + 4 * sb);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            s[j][b][i] = __builtin_amdgcn_exp2f(s[j][b][i]);
-            S.l_part[b][i & 1] = fmaf(s[j][b][i], iv[i], S.l_part[b][i & 1]);
-          }
-          pk[b][sb] = cvt_fp8x4_over(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3], 0);
-          if constexpr (two) {
-            if (ht == 0) p1[j][b] = s[j][b];
-          }
-        }
-      }
-      if constexpr (two) {
-        if (ht == 1) {
-          // both halves' first-term codes are in pk: multiply them, then the
-          // residual codes of both halves
-          pv(kOne);
+          for (int w = 4; w < 8; ++w) pk[b][w] = 0;
+        pv(S, vb, pk, kOne);
+        if constexpr (two) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
+            for (int b = 0; b < NB; ++b)
               pk[b][j] = residual_fp8x4(p1[j][b][0], p1[j][b][1], p1[j][b][2], p1[j][b][3], pk[b][j], 0);
-              pk[b][4 + j] = residual_fp8x4(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3], pk[b][4 + j], 0);
-            }
-          pv(kOne - kLoShift);
+          pv(S, vb, pk, kOne - kLoShift);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pk[b][w] = 0;
+            if constexpr (two) p1[w][b] = v4f{0.f, 0.f, 0.f, 0.f};  // no residual left either
+          }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float m_new = own[b] ? fmaxf(S.m_run[b], tmax[b] + S.msub[b]) : S.m_run[b];
+        const float alpha = !own[b] ? 1.f
+                            : S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - m_new);
+        S.l_part[b][0] *= alpha;
+        S.l_part[b][1] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) S.o[db][b] *= alpha;
+        const float shift = !own[b] || m_new == -INFINITY ? 0.f : m_new - S.msub[b];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[j][b] -= shift;
+        S.m_run[b] = m_new;
+        S.msub[b] = m_new == -INFINITY ? 0.f : m_new;
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sb = 4 * ht + j;
+      const v4f iv = *reinterpret_cast<const v4f*>(tg + kFacIv + 4 * sb);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[j][b][i] = __builtin_amdgcn_exp2f(s[j][b][i]);
+          S.l_part[b][i & 1] = fmaf(s[j][b][i], iv[i], S.l_part[b][i & 1]);
+        }
+        pk[b][sb] = cvt_fp8x4(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3]);
+        if constexpr (two) {
+          if (ht == 0) p1[j][b] = s[j][b];
         }
       }
     }
-    if constexpr (!two) pv(kOne);
+    if constexpr (two) {
+      if (ht == 1) {
+        pv(S, vb, pk, kOne);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            pk[b][j] = residual_fp8x4(p1[j][b][0], p1[j][b][1], p1[j][b][2], p1[j][b][3], pk[b][j], 0);
+            pk[b][4 + j] = residual_fp8x4(s[j][b][0], s[j][b][1], s[j][b][2], s[j][b][3], pk[b][4 + j], 0);
+          }
+        pv(S, vb, pk, kOne - kLoShift);
+      }
+    }
   };
 
-  auto step = [&](auto& S, uint8_t* cur, uint8_t* nxt, float* fcur, float* fnxt, int st)
+  // ---- per step, one barrier, then each wave runs its tile's half-tiles and
+  //      P V, issuing its share of the next tile's direct loads between its QK
+  //      matrix instructions.
+  auto step = [&](auto& S, uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, float* fcur, float* fnxt, int st)
                   __attribute__((always_inline)) {
+    constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
     wait_vm<0>();
     wait_lgkm0();
-    bare_barrier();  // tile st and its tables are visible; every wave is done with `nxt`
+    bare_barrier();  // tile st and its tables are visible; every wave is done with kn / vn
     const bool more = st + 1 < n_steps;
     if (fac_wave && more) {
-      const float ks = m_ks, vs = m_vs;
-      const int kb = m_kb;
+      fac_write(fnxt, m_ks, m_vs, m_kb);
       if (st + 2 < n_steps) meta_load(st + 2, m_ks, m_vs, m_kb);
-      fac_write(fnxt, ks, vs, kb);
     }
     const float* tbl = fcur + kh * kFacWords;
-    const uint8_t* buf = cur + kh * T::bytes;
+    const uint8_t* kb = kc + kh * T::k_bytes;
+    const uint8_t* vb = vc + kh * T::v_bytes;
     bool vis[2], fast[2], hist[2];
     classify(tbl, 0, vis[0], fast[0], hist[0]);
     classify(tbl, 1, vis[1], fast[1], hist[1]);
     if (!wave_active || !has_tile(st, kh) || (!vis[0] && !vis[1])) {
-      if (more) issue(nxt, st + 1);
+      if (more) {
+        issue_k(kn, st + 1);
+        issue_v(vn, st + 1);
+      }
       return;
     }
     // past the last step the loads have no tile of their own: they reload a
     // valid one into the buffer nobody reads, so every wave issues the same
     // loads (the compiler then needs no waits of its own)
-    tile(S, buf, tbl, vis[0] && vis[1] && fast[0] && fast[1], hist,
-         [&](int j) __attribute__((always_inline)) { issue_j(nxt, st + 1, j); });
+    auto dma = [&](int sb) __attribute__((always_inline)) {
+      if (sb < T::dma_instr) issue_j(kn, vn, st + 1, sb);
+    };
+    const bool common = vis[0] && vis[1] && fast[0] && fast[1];
+    v8i pk[NB];
+    v4f p1[4][NB];  // fp32 probabilities of the first half (residual codes)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      v4f s[4][NB];
+      qk_half(S, kb, tbl, ht, s, dma);
+      soft_half(S, tbl, vb, ht, common, hist[ht], s, pk, p1);
+    }
+    if constexpr (NB == 2) pv(S, vb, pk, kOne);
   };
 
   // Merge the two key halves through LDS (the stage buffers are free then)
@@ -709,8 +765,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     for (int b = 0; b < NB; ++b) l_sum[b] = S.l_part[b][0] + S.l_part[b][1];
     __syncthreads();
     constexpr int kXw = 4 + 2 * 4 * NDB;  // words per lane
-    static_assert(2 * kWave * kXw * 4 <= Lds<D>::stage, "merge buffer");
-    float* xch = reinterpret_cast<float*>(wq < 2 ? st0 : st1) + ((wq & 1) * kWave + lane) * kXw;
+    static_assert(kWave * kXw * 4 <= Lds<D>::kstage && kWave * kXw * 4 <= Lds<D>::vstage, "merge buffer");
+    uint8_t* xbuf = wq == 0 ? ks0 : wq == 1 ? ks1 : wq == 2 ? vs0 : vs1;
+    float* xch = reinterpret_cast<float*>(xbuf) + lane * kXw;
     if (kh == 1) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -768,8 +825,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 
   auto run = [&](auto& S) __attribute__((always_inline)) {
     for (int st = 0; st < n_steps; st += 2) {
-      step(S, st0, st1, fac0, fac1, st);
-      if (st + 1 < n_steps) step(S, st1, st0, fac1, fac0, st + 1);
+      step(S, ks0, vs0, ks1, vs1, fac0, fac1, st);
+      if (st + 1 < n_steps) step(S, ks1, vs1, ks0, vs0, fac1, fac0, st + 1);
     }
   };
 
@@ -790,7 +847,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
           meta_load(0, m2_ks, m2_vs, m2_kb);
           meta_load(1, m_ks, m_vs, m_kb);
         }
-        issue(st0, 0);
+        issue_k(ks0, 0);
+        issue_v(vs0, 0);
       }
       BlkState<NDB, 1> S;
       prep_q(S, pass);
