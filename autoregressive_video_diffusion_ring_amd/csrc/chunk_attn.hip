@@ -186,6 +186,19 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(lds_wave_base), 16, 0, 0);
 }
 
+// The same load from a buffer: 32-bit lane offset plus a scalar offset, no
+// 64-bit vector address per load (the tile loads use this form; a raw buffer
+// returns zeros past its end).
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff,
+                                          uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_wave_base), 16, static_cast<int>(off),
+                                           static_cast<int>(soff), 0, 0);
+}
+
 // Direct-to-LDS loads of one tile for one key half.  Every wave of the half
 // moves whole 1 KB blocks (64 lanes x 16 bytes, contiguous in LDS); each lane
 // picks the global chunk that belongs at its LDS position.  The lane's byte
@@ -198,6 +211,8 @@ struct DmaPlan {
   uint32_t k[Tile<KV, D>::k_instr];  // from the tile's first K row
   uint32_t v[Tile<KV, D>::v_instr];  // from V^T[h][0][first slot of the tile]
   const uint8_t* meta;               // this lane's metadata chunk of tile 0
+  __amdgpu_buffer_rsrc_t k_rsrc;     // this head's K rows [v_ld][D]
+  __amdgpu_buffer_rsrc_t v_rsrc;     // this head's V^T rows [D][v_ld]
 };
 
 
@@ -211,6 +226,8 @@ __device__ __forceinline__ DmaPlan<KV, D> dma_plan(const AttnArgs& a, int h, int
   pl.meta = which == 0 ? reinterpret_cast<const uint8_t*>(a.k_scale + hs)
             : which == 1 ? reinterpret_cast<const uint8_t*>(a.v_scale + hs)
                          : reinterpret_cast<const uint8_t*>(a.slot_block + j);
+  pl.k_rsrc = make_rsrc(a.k + static_cast<size_t>(h) * a.v_ld * T::k_row, static_cast<uint32_t>(a.v_ld) * T::k_row);
+  pl.v_rsrc = make_rsrc(a.v + static_cast<size_t>(h) * D * a.v_ld * T::es, static_cast<uint32_t>(D * a.v_ld * T::es));
 #pragma unroll
   for (int j = 0; j < T::k_instr; ++j) {
     const int p = (wq * T::k_instr + j) * kWave + lane;  // LDS chunk index
@@ -232,12 +249,12 @@ __device__ __forceinline__ void issue_part(const AttnArgs& a, const DmaPlan<KV, 
                                            uint8_t* buf, int wq, int j) {
   using T = Tile<KV, D>;
   if (j < T::k_instr) {
-    const uint8_t* kb = a.k + (static_cast<size_t>(h) * a.v_ld + tile * kKT) * T::k_row;
-    dma16(kb + pl.k[j], buf + T::k_off + (wq * T::k_instr + j) * 1024);
+    dma16_buf(pl.k_rsrc, pl.k[j], static_cast<uint32_t>(tile * kKT * T::k_row),
+              buf + T::k_off + (wq * T::k_instr + j) * 1024);
   } else {
     const int jv = j - T::k_instr;
-    const uint8_t* vb = a.v + (static_cast<size_t>(h) * D * a.v_ld + tile * kKT) * T::es;
-    dma16(vb + pl.v[jv], buf + T::v_off + (wq * T::v_instr + jv) * 1024);
+    dma16_buf(pl.v_rsrc, pl.v[jv], static_cast<uint32_t>(tile * kKT * T::es),
+              buf + T::v_off + (wq * T::v_instr + jv) * 1024);
   }
 }
 
