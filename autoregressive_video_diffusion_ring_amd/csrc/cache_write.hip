@@ -342,7 +342,10 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(WriteArgs a) {
 // stores on its own and loads and stores of different waves overlap as in a
 // plain copy:
 //  * K workgroups take (token, head) rows in input order, kKRows per group
-//    of 16 lanes: rotate, quantise and store each row (one d-byte cache row);
+//    of 16 lanes: rotate, quantise and store each row (one d-byte cache row).
+//    The rotation angles depend on the token and the pair only, so a
+//    workgroup computes each (token, pair) cosine and sine once, into LDS,
+//    while its row loads are in flight (every head of a token shares them);
 //  * V workgroups take one head and a 128-slot aligned tile of the written
 //    range, 4 consecutive slots x D/16 values per thread; each thread stores,
 //    for each of its values, the 4 slots' codes as one word of the V^T row,
@@ -355,6 +358,7 @@ constexpr int kVTile = 128;     // slots per V workgroup
 constexpr int kVSlots = 4;      // consecutive slots per thread of a V workgroup
 constexpr int kKRows = 2;       // rows per 16-lane group of a K workgroup
 constexpr int kKRowsPerWg = kWThreadsFp8 / kLanesPerRow * kKRows;
+constexpr int kKTokMax = kKRowsPerWg + 1;  // tokens one K workgroup's rows can span (H >= 1)
 static_assert(kWThreadsFp8 / kLanesPerRow * kVSlots == kVTile, "V tile");
 
 template <int D>
@@ -378,9 +382,25 @@ __global__ __launch_bounds__(kWThreadsFp8) void cache_write_fp8_kernel(WriteArgs
       for (int w = 0; w < Raw<KV_FP8, EPL>::words; ++w) rk[i].w[w] = 0u;
       if (row0 + i < n_rows) load_raw<KV_FP8, EPL>(a.k_new, static_cast<size_t>(row0 + i) * D + piece * EPL, rk[i]);
     }
-    double rev[EPL / 2];
-#pragma unroll
-    for (int e = 0; e < EPL / 2; ++e) rev[e] = a.rope.rev[piece * (EPL / 2) + e];
+    // (cos, sin) of every (token, pair) of this workgroup's rows: the angle
+    // pos * theta_i reduced in float64 to at most half a revolution, then the
+    // hardware sine and cosine (which take revolutions)
+    __shared__ float2 cs_tab[kKTokMax * (D / 2)];
+    const int wg_row0 = blockIdx.x * kKRowsPerWg;
+    const int t_lo = wg_row0 / H;
+    if (a.use_rope) {
+      const int t_hi = min(wg_row0 + kKRowsPerWg, n_rows) - 1;
+      const int n_ang = (t_hi / H - t_lo + 1) * (D / 2);
+      for (int i = tid; i < n_ang; i += kWThreadsFp8) {
+        const int e = i % (D / 2);
+        const long long pos = static_cast<long long>(a.pos0) + t_lo + i / (D / 2);
+        double r = static_cast<double>(pos) * a.rope.rev[e];
+        r -= rint(r);
+        const float tt = static_cast<float>(r);
+        cs_tab[i] = make_float2(__builtin_amdgcn_cosf(tt), __builtin_amdgcn_sinf(tt));
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < kKRows; ++i) {
       const int row = row0 + i;
@@ -388,16 +408,13 @@ __global__ __launch_bounds__(kWThreadsFp8) void cache_write_fp8_kernel(WriteArgs
       float xk[EPL];
       unpack<KV_FP8, EPL>(rk[i], xk);
       if (a.use_rope) {
-        const long long pos = static_cast<long long>(a.pos0) + t;
+        const float2* cs_row = cs_tab + (t - t_lo) * (D / 2) + piece * (EPL / 2);
 #pragma unroll
         for (int e = 0; e < EPL / 2; ++e) {
-          double r = static_cast<double>(pos) * rev[e];
-          r -= rint(r);
-          const float tt = static_cast<float>(r);
-          const float sn = __builtin_amdgcn_sinf(tt), cs = __builtin_amdgcn_cosf(tt);
+          const float2 c = cs_row[e];
           const float x0 = xk[2 * e], x1 = xk[2 * e + 1];
-          xk[2 * e] = x0 * cs - x1 * sn;
-          xk[2 * e + 1] = x0 * sn + x1 * cs;
+          xk[2 * e] = x0 * c.x - x1 * c.y;
+          xk[2 * e + 1] = x0 * c.y + x1 * c.x;
         }
       }
       const float ks = row_scale<kLanesPerRow, EPL>(xk);
