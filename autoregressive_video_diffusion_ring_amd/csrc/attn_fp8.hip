@@ -344,10 +344,12 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     for (int j = T::k_instr; j < T::dma_instr; ++j) issue_j(nullptr, vst, li, j);
   };
 
-  // ---- per-slot metadata for the factor tables.  Wave f of key half 0
-  //      builds table f (half f / 2, half-tile f % 2) of every step: lane L
-  //      handles slot 32 (L / 16) + 16 (f % 2) + L % 16 of the tile.
-  const bool fac_wave = kh == 0;
+  // ---- per-slot metadata for the factor tables.  Table f (half f / 2,
+  //      half-tile f % 2) of every step is built by the two waves with wq =
+  //      f: the key-half-0 wave writes the per-slot factors, the key-half-1
+  //      wave the half-tile summary, so that neither half carries the whole
+  //      table work into the step barrier.  Lane L handles slot
+  //      32 (L / 16) + 16 (f % 2) + L % 16 of the tile.
   const int fh = wq >> 1, fht = wq & 1;
   const int fslot = 32 * g + 16 * fht + n16;
   float m_ks = 0.f, m_vs = 0.f;
@@ -362,13 +364,16 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   const float c_mul = a.scale_log2;
   auto fac_write = [&](float* ftab, float ks, float vs, int kb) __attribute__((always_inline)) {
     float* tbl = ftab + fh * kFacWords;
+    if (kh == 0) {
+      const float vsc = fmaxf(vs, kMinVScale);
+      const float A = fmaxf(c_mul * ks, kMinA);
+      tbl[kFacA + fslot] = A;
+      tbl[kFacC + fslot] = __builtin_amdgcn_logf(vsc) * __builtin_amdgcn_rcpf(A);
+      tbl[kFacIv + fslot] = __builtin_amdgcn_rcpf(vsc);
+      reinterpret_cast<int32_t*>(tbl)[kFacKb + fslot] = kb;
+      return;
+    }
     const bool kval = kb != -1;
-    const float vsc = fmaxf(vs, kMinVScale);
-    const float A = fmaxf(c_mul * ks, kMinA);
-    tbl[kFacA + fslot] = A;
-    tbl[kFacC + fslot] = __builtin_amdgcn_logf(vsc) * __builtin_amdgcn_rcpf(A);
-    tbl[kFacIv + fslot] = __builtin_amdgcn_rcpf(vsc);
-    reinterpret_cast<int32_t*>(tbl)[kFacKb + fslot] = kb;
     const uint64_t vb = __ballot(kval);
     const int kmin = wave_minmax_i32<false>(kval ? kb : INT32_MAX);
     const int kmax = wave_minmax_i32<true>(kval ? kb : INT32_MIN);
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   const double rev_lane = wave == 0 && lane < D / 2 ? a.rope.rev[lane] : 0.0;
   float m2_ks = 0.f, m2_vs = 0.f;
   int m2_kb = -1;
-  meta_load(0, m2_ks, m2_vs, m2_kb);  // every wave loads (same load history); half 0 uses them
+  meta_load(0, m2_ks, m2_vs, m2_kb);  // every wave builds a part of the tables
   meta_load(1, m_ks, m_vs, m_kb);
   constexpr int kQLoads = 4;  // 16-byte loads per block: d = 32 g .. 32 g + 31 as bf16
   v4u qraw[2][kQLoads];
@@ -720,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     wait_lgkm0();
     bare_barrier();  // tile st and its tables are visible; every wave is done with kn / vn
     const bool more = st + 1 < n_steps;
-    if (fac_wave && more) {
+    if (more) {
       fac_write(fnxt, m_ks, m_vs, m_kb);
       if (st + 2 < n_steps) meta_load(st + 2, m_ks, m_vs, m_kb);
     }
@@ -833,7 +838,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   if constexpr (!TWO) {
     BlkState<NDB, 2> S;
     prep_q(S, 0);
-    if (fac_wave) fac_write(fac0, m2_ks, m2_vs, m2_kb);
+    fac_write(fac0, m2_ks, m2_vs, m2_kb);
     run(S);
     finish(S, 0);
   } else {
@@ -843,16 +848,14 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
         // restart the tile pipeline for the second query block (every wave
         // is past the merge, so the stage buffers are free)
         __syncthreads();
-        if (fac_wave) {
-          meta_load(0, m2_ks, m2_vs, m2_kb);
-          meta_load(1, m_ks, m_vs, m_kb);
-        }
+        meta_load(0, m2_ks, m2_vs, m2_kb);
+        meta_load(1, m_ks, m_vs, m_kb);
         issue_k(ks0, 0);
         issue_v(vs0, 0);
       }
       BlkState<NDB, 1> S;
       prep_q(S, pass);
-      if (fac_wave) fac_write(fac0, m2_ks, m2_vs, m2_kb);
+      fac_write(fac0, m2_ks, m2_vs, m2_kb);
       run(S);
       finish(S, pass);
     }
