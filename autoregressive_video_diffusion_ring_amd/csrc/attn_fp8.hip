@@ -43,8 +43,8 @@
 #include <cmath>
 #include <type_traits>
 
-#include "rc_device.h"
-#include "rc_kernels.h"
+#include "/root/repo/autoregressive_video_diffusion_ring_amd/csrc/rc_device.h"
+#include "/root/repo/autoregressive_video_diffusion_ring_amd/csrc/rc_kernels.h"
 
 namespace rc {
 namespace {
@@ -501,9 +501,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   qb_hi = __builtin_amdgcn_readfirstlane(wave_minmax_i32<true>(qb_hi));
   const bool same_block = GEN && a.same_block != 0;
 
-  // Wave-uniform class of half-tile ht from its summary.
-  auto classify = [&](const float* tbl, int ht, bool& vis, bool& fast, bool& hist) __attribute__((always_inline)) {
-    const v4i sm = *reinterpret_cast<const v4i*>(tbl + kFacSum + 4 * ht);
+  // Wave-uniform class of half-tile ht from its summary sm (read from the
+  // tables at kFacSum + 4 ht).
+  auto classify = [&](const v4i sm, bool& vis, bool& fast, bool& hist) __attribute__((always_inline)) {
     const int any = __builtin_amdgcn_readfirstlane(sm.x);
     const int all = __builtin_amdgcn_readfirstlane(sm.y);
     const int kmin = __builtin_amdgcn_readfirstlane(sm.z);
@@ -725,16 +725,20 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     wait_lgkm0();
     bare_barrier();  // tile st and its tables are visible; every wave is done with kn / vn
     const bool more = st + 1 < n_steps;
+    const float* tbl = fcur + kh * kFacWords;
+    const uint8_t* kb = kc + kh * T::k_bytes;
+    const uint8_t* vb = vc + kh * T::v_bytes;
+    // the summaries are read before the next tile's table work, which then
+    // covers their latency
+    const v4i sm0 = *reinterpret_cast<const v4i*>(tbl + kFacSum);
+    const v4i sm1 = *reinterpret_cast<const v4i*>(tbl + kFacSum + 4);
     if (more) {
       fac_write(fnxt, m_ks, m_vs, m_kb);
       if (st + 2 < n_steps) meta_load(st + 2, m_ks, m_vs, m_kb);
     }
-    const float* tbl = fcur + kh * kFacWords;
-    const uint8_t* kb = kc + kh * T::k_bytes;
-    const uint8_t* vb = vc + kh * T::v_bytes;
     bool vis[2], fast[2], hist[2];
-    classify(tbl, 0, vis[0], fast[0], hist[0]);
-    classify(tbl, 1, vis[1], fast[1], hist[1]);
+    classify(sm0, vis[0], fast[0], hist[0]);
+    classify(sm1, vis[1], fast[1], hist[1]);
     if (!wave_active || !has_tile(st, kh) || (!vis[0] && !vis[1])) {
       if (more) {
         issue_k(kn, st + 1);
