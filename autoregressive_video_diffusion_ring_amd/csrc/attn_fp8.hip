@@ -43,8 +43,8 @@
 #include <cmath>
 #include <type_traits>
 
-#include "/root/repo/autoregressive_video_diffusion_ring_amd/csrc/rc_device.h"
-#include "/root/repo/autoregressive_video_diffusion_ring_amd/csrc/rc_kernels.h"
+#include "rc_device.h"
+#include "rc_kernels.h"
 
 namespace rc {
 namespace {
@@ -295,7 +295,11 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
   const int n_local = (max(t_end - t_begin, 0) + 1) / 2;  // steps (tiles per half, rounded up)
-  auto tile_of = [&](int li, int half) { return t_begin + 2 * li + half; };
+  // key half 1 takes the even tiles, key half 0 the odd ones: with an even
+  // tile count the last tile, partly empty and masked when the ring is full,
+  // goes to the key half whose waves issue first, so the two halves end
+  // their loops closer together
+  auto tile_of = [&](int li, int half) { return t_begin + 2 * li + (1 - half); };
   auto has_tile = [&](int li, int half) { return li < n_local && tile_of(li, half) < t_end; };
   const int t_safe = min(t_begin, a.n_tiles - 1);
 
@@ -426,6 +430,59 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   //      operands (the blocks S holds; with NB = 1 also the residual codes)
   auto prep_q = [&](auto& S, int b0) __attribute__((always_inline)) {
     constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
+    if constexpr (NB == 2) {
+      // the waves wq of the two key halves hold the same queries: the wave of
+      // key half kh rotates and quantises block kh only and takes the other
+      // block's operands from its partner through LDS (the second stage
+      // buffers, free until the first step issues its loads)
+      const int bq = kh;
+      const long long qpos = static_cast<long long>(a.q_pos0) + (bq ? qi[1] : qi[0]);
+      const bool live = (bq ? q_ok[1] : q_ok[0]) && g < NG;
+      float xb[32];
+#pragma unroll
+      for (int e = 0; e < 32; e += 2) {
+        const uint32_t w = bq ? qraw[1][e / 8][(e / 2) % 4] : qraw[0][e / 8][(e / 2) % 4];
+        const float x0 = __uint_as_float(w << 16);
+        const float x1 = __uint_as_float(w & 0xFFFF0000u);
+        float c, sn;
+        rope_cs_hw(rev_lds[(32 * (g % NG) + e) >> 1], qpos, &c, &sn);
+        xb[e] = live ? x0 * c - x1 * sn : 0.f;
+        xb[e + 1] = live ? x0 * sn + x1 * c : 0.f;
+      }
+      float am0 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) am0 = fmaxf(am0, fabsf(xb[e]));
+      float am1 = am0;
+      across_groups<true>(am0, am1);
+      const int bexp = static_cast<int>((__float_as_uint(am0) >> 23) & 0xFF);
+      const int code = am0 > 0.f ? max(bexp - 7, 1) : kOne;
+      const float inv = __uint_as_float(static_cast<uint32_t>(254 - code) << 23);
+      v8i own;
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        own[w] = cvt_fp8x4_over(xb[4 * w] * inv, xb[4 * w + 1] * inv, xb[4 * w + 2] * inv, xb[4 * w + 3] * inv, 0);
+      // exchange: 8 operand words per (wave wq, block, lane) in the second K
+      // stage, the scale codes in the second V stage
+      int32_t* xq = reinterpret_cast<int32_t*>(ks1);
+      int32_t* xc = reinterpret_cast<int32_t*>(vs1);
+      static_assert(kQSub * 2 * kWave * 32 <= Lds<D>::kstage && kQSub * 2 * kWave * 4 <= Lds<D>::vstage,
+                    "Q exchange");
+      const int own_slot = (wq * 2 + bq) * kWave + lane;
+      const int oth_slot = (wq * 2 + 1 - bq) * kWave + lane;
+      *reinterpret_cast<v8i*>(xq + 8 * own_slot) = own;
+      xc[own_slot] = code;
+      wait_lgkm0();
+      bare_barrier();  // both blocks' operands are in LDS
+      const v8i oth = *reinterpret_cast<const v8i*>(xq + 8 * oth_slot);
+      const int oth_code = xc[oth_slot];
+      S.qf[0] = bq == 0 ? own : oth;
+      S.qf[1] = bq == 0 ? oth : own;
+      S.qsc[0] = bq == 0 ? code : oth_code;
+      S.qsc[1] = bq == 0 ? oth_code : code;
+      S.qb[0] = my_qb[0];
+      S.qb[1] = my_qb[1];
+      return;
+    }
     float x[NB][32];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -766,38 +823,58 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
 
   // Merge the two key halves through LDS (the stage buffers are free then)
   // and store the outputs of the blocks in `S` (block b of S is query block
-  // b0 + b of the wave).
+  // b0 + b of the wave).  Each key half finishes half of the d blocks: it
+  // hands its stabilisers, sums and the other half's O to its partner and
+  // takes the partner's for its own half, so both waves of a pair share the
+  // merge and the stores.
   auto finish = [&](auto& S, int b0) __attribute__((always_inline)) {
     constexpr int NB = std::remove_reference_t<decltype(S)>::nb;
+    constexpr int kHd = NDB / 2;           // d blocks per key half
+    constexpr int kXh = 4 + 8 * kHd;       // words one key half hands over, per lane
+    constexpr int kXw = 2 * kXh + 4;       // per lane (padded against bank conflicts)
+    static_assert(kWave * kXw * 4 <= Lds<D>::kstage && kWave * kXw * 4 <= Lds<D>::vstage, "merge buffer");
     float l_sum[2];
 #pragma unroll
     for (int b = 0; b < NB; ++b) l_sum[b] = S.l_part[b][0] + S.l_part[b][1];
     __syncthreads();
-    constexpr int kXw = 4 + 2 * 4 * NDB;  // words per lane
-    static_assert(kWave * kXw * 4 <= Lds<D>::kstage && kWave * kXw * 4 <= Lds<D>::vstage, "merge buffer");
     uint8_t* xbuf = wq == 0 ? ks0 : wq == 1 ? ks1 : wq == 2 ? vs0 : vs1;
     float* xch = reinterpret_cast<float*>(xbuf) + lane * kXw;
-    if (kh == 1) {
+    // key half kh finishes d blocks kh kHd .. kh kHd + kHd - 1 and hands over
+    // the others.  The accumulators are chosen by value (a wave-uniform
+    // select per register), never by a computed index, so they stay in
+    // registers.
+    const bool k0 = kh == 0;
+    {
+      float* w = xch + (k0 ? 0 : kXh);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        xch[b] = S.m_run[b];
-        xch[2 + b] = l_sum[b];
+        w[b] = S.m_run[b];
+        w[2 + b] = l_sum[b];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) *reinterpret_cast<v4f*>(xch + 4 + 8 * db + 4 * b) = S.o[db][b];
+        for (int i = 0; i < kHd; ++i)
+          *reinterpret_cast<v4f*>(w + 4 + 8 * i + 4 * b) = k0 ? S.o[kHd + i][b] : S.o[i][b];
       }
     }
     __syncthreads();
-    if (kh == 1 || !wave_active) return;
+    if (!wave_active) return;
+    // every read first (one wait for all of them), then the arithmetic
+    const float* r = xch + (k0 ? kXh : 0);
+    const v4f ml = *reinterpret_cast<const v4f*>(r);
+    v4f ox[kHd][NB];
+#pragma unroll
+    for (int i = 0; i < kHd; ++i)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ox[i][b] = *reinterpret_cast<const v4f*>(r + 4 + 8 * i + 4 * b);
+    v4f mine[kHd][NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float m1 = xch[b], l1 = xch[2 + b];
+      const float m1 = ml[b], l1 = ml[2 + b];
       const float mm = fmaxf(S.m_run[b], m1);
       const float a0 = S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - mm);
       const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
       l_sum[b] = a0 * l_sum[b] + a1 * l1;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        S.o[db][b] = a0 * S.o[db][b] + a1 * *reinterpret_cast<const v4f*>(xch + 4 + 8 * db + 4 * b);
+      for (int i = 0; i < kHd; ++i) mine[i][b] = a0 * (k0 ? S.o[i][b] : S.o[kHd + i][b]) + a1 * ox[i][b];
       S.m_run[b] = mm;
     }
     // the lane holds d = 16 db + 4 g + 0..3 of its queries
@@ -807,6 +884,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       float t1 = l_sum[0];
       across_groups<false>(l_sum[0], t1);
     }
+    const int d0 = (k0 ? 0 : 16 * kHd) + 4 * g;  // first d of the lane's stores
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int qq = (b0 + b) ? qi[1] : qi[0];
@@ -815,19 +893,18 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       const float osc = any ? 1.f / l_sum[b] : 0.f;
       const float lse_v = any ? (S.m_run[b] + __log2f(l_sum[b])) * kLn2 : -INFINITY;
       if (a.n_splits == 1) {
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(qq) * a.H + h) * D;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(qq) * a.H + h) * D + d0;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v4f r = S.o[db][b] * osc;
-          *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) =
-              make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+        for (int i = 0; i < kHd; ++i) {
+          const v4f r4 = mine[i][b] * osc;
+          *reinterpret_cast<uint2*>(orow + 16 * i) = make_uint2(pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3]));
         }
-        if (a.lse && g == 0) a.lse[static_cast<size_t>(h) * a.n_q + qq] = lse_v;
+        if (k0 && a.lse && g == 0) a.lse[static_cast<size_t>(h) * a.n_q + qq] = lse_v;
       } else {
-        float* po = a.part_o + ((static_cast<size_t>(split) * a.n_q + qq) * a.H + h) * D;
+        float* po = a.part_o + ((static_cast<size_t>(split) * a.n_q + qq) * a.H + h) * D + d0;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) *reinterpret_cast<v4f*>(po + 16 * db + 4 * g) = S.o[db][b] * osc;
-        if (g == 0) a.part_lse[(static_cast<size_t>(split) * a.H + h) * a.n_q + qq] = lse_v;
+        for (int i = 0; i < kHd; ++i) *reinterpret_cast<v4f*>(po + 16 * i) = mine[i][b] * osc;
+        if (k0 && g == 0) a.part_lse[(static_cast<size_t>(split) * a.H + h) * a.n_q + qq] = lse_v;
       }
     }
   };
