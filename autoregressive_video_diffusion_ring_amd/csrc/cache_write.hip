@@ -550,8 +550,19 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
       float x[EPT];
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
       if constexpr (KV == KV_FP8) {
+        // FP8 rows are rotated in code units (two codes per conversion): the
+        // old scale s cancels from the new codes, round(R(c s) / (s max|R c| /
+        // 448)) = round(R c / (max|R c| / 448)), and enters only the new
+        // scale s max|R c| / 448
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) x[e] = fp8_to_f32(w[e / 4], e % 4) * sc[i];
+        for (int e = 0; e < EPT / 4; ++e) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[e]), false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[e]), true);
+          x[4 * e] = lo[0];
+          x[4 * e + 1] = lo[1];
+          x[4 * e + 2] = hi[0];
+          x[4 * e + 3] = hi[1];
+        }
       } else if constexpr (KV == KV_BF16) {
 #pragma unroll
         for (int e = 0; e < EPT / 2; ++e) {
@@ -570,8 +581,9 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
       }
       float nsc = 0.f, rc = 0.f;
       if constexpr (KV == KV_FP8) {
-        nsc = row_scale<LPR, EPT>(x);
-        rc = scale_rcp(nsc);
+        const float csc = row_scale<LPR, EPT>(x);  // max|R c| / 448
+        rc = scale_rcp(csc);
+        nsc = csc * sc[i];
       }
       if (!live[i]) continue;  // whole rows skip together (after the row's shuffles)
       store_row<KV, EPT, false>(r.k, srow * D + lane * EPT, x, nsc, rc);  // rotated in float32
