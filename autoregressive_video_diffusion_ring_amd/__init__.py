@@ -26,6 +26,7 @@ from ._lib import (DTYPES, RC_BF16, RC_F32, RC_FP8_E4M3, RC_MASK_BLOCK_CAUSAL, R
 __all__ = [
     "Ring", "RcError", "RcRing", "rc_ring_init", "rc_cache_write", "rc_cache_rerotate",
     "rc_chunk_attention", "rc_ring_advance", "rc_attention_workspace_bytes", "rc_debug_visibility",
+    "rc_debug_tile_classes", "rc_debug_tile_classes_bytes",
     "rc_chunk_attention_noalloc", "rc_attention_noalloc_limit",
     "rc_ring_sizes", "rc_ring_v_ld", "rc_key_mass", "rc_key_mass_slots", "rc_key_mass_workspace_bytes",
     "rc_cache_write_scored",
@@ -174,6 +175,16 @@ def rc_debug_visibility(ring: RcRing, n_q: int, q_block0: int, q_block_len: int,
                                     _stream(stream)))
 
 
+def rc_debug_tile_classes_bytes(ring: RcRing, n_q: int) -> int:
+    return lib().rc_debug_tile_classes_bytes(ctypes.byref(ring), n_q)
+
+
+def rc_debug_tile_classes(ring: RcRing, n_q: int, q_block0: int, q_block_len: int, mask: int, cache_bias: float,
+                          classes, classes_bytes: int, stream=None) -> None:
+    check(lib().rc_debug_tile_classes(ctypes.byref(ring), n_q, q_block0, q_block_len, mask, float(cache_bias),
+                                      _ptr(classes), classes_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------------ owner
 class Ring:
     """One layer's ring cache: device buffers as torch tensors plus the
@@ -317,6 +328,17 @@ class Ring:
         mask = torch.empty((n_q, self.N), dtype=torch.uint8, device=self.device)
         rc_debug_visibility(self.struct, n_q, q_block0, q_block_len, mask, stream)
         return mask
+
+    def tile_classes(self, n_q: int, q_block0: int, q_block_len: int, cache_bias: float = 0.0,
+                     same_block: bool = False, stream=None):
+        """The FP8 attention kernel's half-tile classes, uint8 [ceil(n_q/32)][ceil(N/128)][2]
+        (bits: 1 vis, 2 fast, 4 hist)."""
+        shape = ((n_q + 31) // 32, (self.N + 127) // 128, 2)
+        classes = torch.empty(shape, dtype=torch.uint8, device=self.device)
+        rc_debug_tile_classes(self.struct, n_q, q_block0, q_block_len,
+                              RC_MASK_SAME_BLOCK if same_block else RC_MASK_BLOCK_CAUSAL, cache_bias, classes,
+                              classes.numel(), stream)
+        return classes
 
     # ---- read-back in the logical layout [H][N][d] (copies, for checking)
     def _view(self, i, dtype, shape):

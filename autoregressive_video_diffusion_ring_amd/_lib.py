@@ -71,6 +71,9 @@ SIGNATURES = {
                                         c_float, c_void_p, c_size_t, c_void_p]),
     "rc_cache_write_scored_workspace_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
     "rc_debug_visibility": (c_int32, [POINTER(RcRing), c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "rc_debug_tile_classes_bytes": (c_size_t, [POINTER(RcRing), c_int32]),
+    "rc_debug_tile_classes": (c_int32, [POINTER(RcRing), c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
+                                        c_size_t, c_void_p]),
     "rc_last_error": (c_char_p, []),
 }
 

@@ -235,6 +235,36 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return static_cast<int>(r32[0]) + static_cast<int>(r32[1]);
 }
 
+// Summary of a half-tile from the block ids of its 64 slots, one per lane
+// (-1 = empty): {any slot valid, all valid, min block, max block over the
+// valid slots}.
+__device__ __forceinline__ v4i half_tile_summary(int kb) {
+  const bool kval = kb != -1;
+  const uint64_t vb = __ballot(kval);
+  const int kmin = wave_minmax_i32<false>(kval ? kb : INT32_MAX);
+  const int kmax = wave_minmax_i32<true>(kval ? kb : INT32_MIN);
+  return v4i{vb != 0ull ? 1 : 0, vb == ~0ull ? 1 : 0, kmin, kmax};
+}
+
+// Class of a half-tile (summary any, all, kmin, kmax) for a wave whose
+// queries' blocks span qb_lo .. qb_hi.  vis: some slot may be visible to some
+// query (exact under the block-causal mask, a superset under the same-block
+// mask); fast: every slot is visible to every query with one bias value (or
+// the bias is 0), so the per-score mask is skipped; hist: fast with the bias
+// on every score.
+struct HalfTileClass {
+  bool vis, fast, hist;
+};
+__device__ __forceinline__ HalfTileClass half_tile_class(int any, int all, int kmin, int kmax, int qb_lo, int qb_hi,
+                                                         bool same_block, bool bias_zero) {
+  const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
+  if (same_block) return {any && kmin <= qb_hi && kmax >= qb_lo, all_same, false};
+  const bool all_vis = all && kmax <= qb_lo;
+  const bool all_hist = all && kmax < qb_lo;
+  const bool fast = all_vis && (all_hist || all_same || bias_zero);
+  return {any && kmin <= qb_hi, fast, fast && all_hist};
+}
+
 // Softmax state and Q operands of the query blocks one pass handles: NB = 2
 // (both 16-query blocks of the wave, one FP8 term) or 1 (one block, with the
 // residual term of Q).
@@ -377,12 +407,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       reinterpret_cast<int32_t*>(tbl)[kFacKb + fslot] = kb;
       return;
     }
-    const bool kval = kb != -1;
-    const uint64_t vb = __ballot(kval);
-    const int kmin = wave_minmax_i32<false>(kval ? kb : INT32_MAX);
-    const int kmax = wave_minmax_i32<true>(kval ? kb : INT32_MIN);
-    if (lane == 0)
-      *reinterpret_cast<v4i*>(tbl + kFacSum + 4 * fht) = v4i{vb != 0ull ? 1 : 0, vb == ~0ull ? 1 : 0, kmin, kmax};
+    const v4i sm = half_tile_summary(kb);
+    if (lane == 0) *reinterpret_cast<v4i*>(tbl + kFacSum + 4 * fht) = sm;
   };
 
   // ---- queries of this lane: block b (0, 1) holds query wq * 32 + 16 b + n16
@@ -565,18 +591,10 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
     const int all = __builtin_amdgcn_readfirstlane(sm.y);
     const int kmin = __builtin_amdgcn_readfirstlane(sm.z);
     const int kmax = __builtin_amdgcn_readfirstlane(sm.w);
-    const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
-    if (same_block) {
-      vis = any && kmin <= qb_hi && kmax >= qb_lo;
-      fast = all_same;
-      hist = false;
-      return;
-    }
-    vis = any && kmin <= qb_hi;
-    const bool all_vis = all && kmax <= qb_lo;
-    const bool all_hist = all && kmax < qb_lo;
-    fast = all_vis && (all_hist || all_same || a.bias_log2 == 0.f);
-    hist = fast && all_hist;
+    const HalfTileClass c = half_tile_class(any, all, kmin, kmax, qb_lo, qb_hi, same_block, a.bias_log2 == 0.f);
+    vis = c.vis;
+    fast = c.fast;
+    hist = c.hist;
   };
 
   const int n_steps = n_local;
@@ -973,6 +991,28 @@ __global__ __launch_bounds__(256) void combine_fp8_kernel(const float* part_o, c
   if (lse && lane == 0) lse[static_cast<size_t>(h) * n_q + qi] = mx == -INFINITY ? -INFINITY : mx + logf(wsum);
 }
 
+// One wave per (query wave w, tile t, half-tile ht) of an FP8 attention call
+// over the whole ring: the class the attention kernel gives that half-tile,
+// from the same summary and rules (the wave's 32 queries 32 w .. 32 w + 31,
+// their blocks q_block0 + q / q_block_len), as bits vis | fast << 1 | hist << 2.
+__global__ __launch_bounds__(kWave) void tile_class_kernel(const int32_t* slot_block, int n_tiles, int n_q,
+                                                           int q_block0, int q_block_len, int same_block,
+                                                           int bias_zero, uint8_t* out) {
+  const int lane = threadIdx.x;
+  const int item = blockIdx.x;
+  const int ht = item & 1;
+  const int t = (item >> 1) % n_tiles;
+  const int w = (item >> 1) / n_tiles;
+  const v4i sm = half_tile_summary(slot_block[t * kT + 32 * (lane >> 4) + 16 * ht + (lane & 15)]);
+  int lo = INT32_MAX, hi = INT32_MIN;
+  const int q = kQW * w + (lane & (kQW - 1));
+  if (q < n_q) lo = hi = q_block0 + q / q_block_len;
+  lo = wave_minmax_i32<false>(lo);
+  hi = wave_minmax_i32<true>(hi);
+  const HalfTileClass c = half_tile_class(sm.x, sm.y, sm.z, sm.w, lo, hi, same_block != 0, bias_zero != 0);
+  if (lane == 0) out[item] = static_cast<uint8_t>((c.vis ? 1 : 0) | (c.fast ? 2 : 0) | (c.hist ? 4 : 0));
+}
+
 template <int D>
 hipError_t fp8_impl(const RingView& r, const AttnCall& c, int splits, hipStream_t s) {
   F8Args a{};
@@ -1036,6 +1076,22 @@ int fp8_attention_splits(const RingView& r, int n_q) {
   int splits = 1;
   while (items * splits * 2 <= 256 && (splits * 2) * 4 <= n_tiles) splits *= 2;
   return splits;
+}
+
+size_t debug_tile_classes_bytes(const RingView& r, int n_q) {
+  return static_cast<size_t>((n_q + kQW - 1) / kQW) * ((r.N + kT - 1) / kT) * 2;
+}
+
+hipError_t launch_debug_tile_classes(const RingView& r, int n_q, int q_block0, int q_block_len, bool same_block,
+                                     float cache_bias, uint8_t* out, hipStream_t s) {
+  const int n_tiles = (r.N + kT - 1) / kT;
+  const long long items = 2LL * n_tiles * ((n_q + kQW - 1) / kQW);
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  // the attention kernel's test: its bias in log2 units is exactly zero
+  const float bias_log2 = (same_block ? 0.f : cache_bias) * kLog2e;
+  hipLaunchKernelGGL(tile_class_kernel, dim3(static_cast<unsigned>(items)), dim3(kWave), 0, s, r.slot_block, n_tiles,
+                     n_q, q_block0, q_block_len, same_block ? 1 : 0, bias_log2 == 0.f ? 1 : 0, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_attention(const RingView& r, const AttnCall& c, int splits, hipStream_t s) {

@@ -511,6 +511,27 @@ rc_status rc_debug_visibility(const rc_ring* r, int32_t n_q, int32_t q_block0, i
   return ok();
 }
 
+size_t rc_debug_tile_classes_bytes(const rc_ring* r, int32_t n_q) {
+  if (check_ring(r) != RC_OK || n_q < 1) return 0;
+  return rc::debug_tile_classes_bytes(view(r), n_q);
+}
+
+rc_status rc_debug_tile_classes(const rc_ring* r, int32_t n_q, int32_t q_block0, int32_t q_block_len, int32_t mask,
+                                float cache_bias, uint8_t* classes, size_t classes_bytes, void* stream) {
+  rc_status st = check_ring(r);
+  if (st != RC_OK) return st;
+  if (!classes) return fail(RC_ERR_ARG, "classes is NULL");
+  if (n_q < 1 || q_block_len < 1) return fail(RC_ERR_ARG, "n_q and q_block_len must be >= 1");
+  if (mask != RC_MASK_BLOCK_CAUSAL && mask != RC_MASK_SAME_BLOCK) return fail(RC_ERR_ARG, "unknown mask %d", mask);
+  if (!std::isfinite(cache_bias)) return fail(RC_ERR_ARG, "cache_bias must be finite");
+  const size_t need = rc::debug_tile_classes_bytes(view(r), n_q);
+  if (classes_bytes < need) return fail(RC_ERR_ARG, "classes holds %zu bytes, %zu needed", classes_bytes, need);
+  hipError_t e = rc::launch_debug_tile_classes(view(r), n_q, q_block0, q_block_len, mask == RC_MASK_SAME_BLOCK,
+                                               cache_bias, classes, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "tile classes");
+  return ok();
+}
+
 const char* rc_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -55,6 +55,10 @@ hipError_t launch_chunk_attention(const RingView& r, const AttnCall& c, hipStrea
 // FP8 rings (attn_fp8.hip): key splits for n_q queries and the launch.
 int fp8_attention_splits(const RingView& r, int n_q);
 hipError_t launch_fp8_attention(const RingView& r, const AttnCall& c, int splits, hipStream_t s);
+// The FP8 attention kernel's half-tile classes (export for checking).
+size_t debug_tile_classes_bytes(const RingView& r, int n_q);
+hipError_t launch_debug_tile_classes(const RingView& r, int n_q, int q_block0, int q_block_len, bool same_block,
+                                     float cache_bias, uint8_t* out, hipStream_t s);
 
 // Attention mass per head and slot (memory.hip), optionally only for the
 // slots of up to kMassRanges ranges [lo, hi) (ranges: lo, hi pairs on the

@@ -400,6 +400,28 @@ size_t rc_qkv_workspace_bytes(int32_t n, int32_t C);
 rc_status rc_debug_visibility(const rc_ring* ring, int32_t n_q, int32_t q_block0,
                               int32_t q_block_len, uint8_t* mask, void* stream);
 
+/*
+ * The FP8 attention kernel's own tile classes, exported for checking (the
+ * decision that lets it skip the per-score mask; the masks themselves are
+ * rc_chunk_attention's and rc_chunk_attention_ex's, defined there).  For a
+ * call with n_q queries in blocks q_block0 + i / q_block_len, under mask
+ * (RC_MASK_BLOCK_CAUSAL or RC_MASK_SAME_BLOCK) and cache_bias, over the whole
+ * ring: classes (device uint8 [ceil(n_q / 32)][ceil(N / 128)][2]) holds for
+ * each 32-query wave w, 128-slot tile t and half-tile h (the 64 slots
+ * 128 t + 32 g + 16 h + 0..15, g = 0..3) the bits
+ *   1  vis:  some slot may be visible to some query of the wave (exact under
+ *            the block-causal mask; a superset under the same-block mask);
+ *   2  fast: every slot is visible to every query of the wave with one bias
+ *            value (or cache_bias is 0): the per-score mask is skipped;
+ *   4  hist: fast, with the bias on every score.
+ * classes_bytes >= rc_debug_tile_classes_bytes(ring, n_q), else RC_ERR_ARG;
+ * RC_ERR_ARG also for a bad mask, a non-finite bias, n_q or q_block_len < 1.
+ */
+size_t rc_debug_tile_classes_bytes(const rc_ring* ring, int32_t n_q);
+rc_status rc_debug_tile_classes(const rc_ring* ring, int32_t n_q, int32_t q_block0, int32_t q_block_len,
+                                int32_t mask, float cache_bias, uint8_t* classes, size_t classes_bytes,
+                                void* stream);
+
 /* Thread-local description of the last error (empty string if none). */
 const char* rc_last_error(void);
 

@@ -65,6 +65,12 @@ hipError_t launch_qkv_project_write(const RingView&, const void*, int, int, cons
   return launched();
 }
 hipError_t launch_debug_visibility(const RingView&, int, int, int, uint8_t*, hipStream_t) { return launched(); }
+size_t debug_tile_classes_bytes(const RingView& r, int n_q) {
+  return static_cast<size_t>((n_q + 31) / 32) * ((r.N + 127) / 128) * 2;
+}
+hipError_t launch_debug_tile_classes(const RingView&, int, int, int, bool, float, uint8_t*, hipStream_t) {
+  return launched();
+}
 }  // namespace rc
 
 // ---------------------------------------------------------------- helpers
@@ -256,6 +262,19 @@ static void attention_and_mass() {
   CHECK(rc_key_mass_slots(&r, q, 10, 0, 0, 10, 0.f, 0.f, lse, ranges, 2, mass, ws, need, nullptr) == RC_OK);
   CHECK(rc_chunk_attention(&r, q, 10, 0, 0, 10, -0.5f, 0.f, out, lse, ws, 1 << 12, nullptr) == RC_OK);
   REJECT(&r, RC_ERR_ARG, rc_debug_visibility(&r, 10, 0, 10, nullptr, nullptr));
+  // tile classes: size, then each rejection
+  const size_t cls_bytes = rc_debug_tile_classes_bytes(&r, 40);
+  CHECK(cls_bytes == 2 * ((r.n_slots + 127) / 128) * 2);
+  CHECK(rc_debug_tile_classes_bytes(&r, 0) == 0);
+  uint8_t* cls = static_cast<uint8_t*>(g_buf.at(32768));
+  CHECK(rc_debug_tile_classes(&r, 40, 0, 10, RC_MASK_BLOCK_CAUSAL, -0.5f, cls, cls_bytes, nullptr) == RC_OK);
+  CHECK(rc_debug_tile_classes(&r, 40, 0, 10, RC_MASK_SAME_BLOCK, 0.f, cls, cls_bytes, nullptr) == RC_OK);
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 40, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.f, nullptr, cls_bytes, nullptr));
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 40, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.f, cls, cls_bytes - 1, nullptr));
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 0, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.f, cls, cls_bytes, nullptr));
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 40, 0, 0, RC_MASK_BLOCK_CAUSAL, 0.f, cls, cls_bytes, nullptr));
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 40, 0, 10, 7, 0.f, cls, cls_bytes, nullptr));
+  REJECT(&r, RC_ERR_ARG, rc_debug_tile_classes(&r, 40, 0, 10, RC_MASK_BLOCK_CAUSAL, NAN, cls, cls_bytes, nullptr));
 }
 
 static void scored_and_projection() {

@@ -715,6 +715,67 @@ def test_visibility_export_bit_exact():
         assert np.array_equal(m, want), (n_q, b0, bl)
 
 
+def _tile_classes_ref(slot_block, n_q, q_block0, q_block_len, cache_bias, same):
+    """Half-tile classes from the visibility definition: for each 32-query wave,
+    128-slot tile and half-tile (slots 32 g + 16 h + 0..15 of the tile), bit 1
+    if some pair is visible, 2 if every pair is visible with one bias value
+    (or the bias is 0), 4 if that value is the bias on every pair."""
+    N = len(slot_block)
+    n_t, n_w = -(-N // 128), -(-n_q // 32)
+    sb = np.full(n_t * 128, -1, dtype=np.int64)
+    sb[:N] = slot_block
+    vis, earlier = visibility(sb, query_blocks(n_q, q_block0, q_block_len), "same" if same else "causal")
+    bias_zero = same or cache_bias == 0.0
+    out = np.zeros((n_w, n_t, 2), dtype=np.uint8)
+    for w in range(n_w):
+        qs = slice(32 * w, min(32 * w + 32, n_q))
+        for t in range(n_t):
+            for h in range(2):
+                cols = [128 * t + 32 * g + 16 * h + i for g in range(4) for i in range(16)]
+                v, e = vis[qs][:, cols], earlier[qs][:, cols]
+                fast = bool(v.all()) and (bool(e.all()) or not e.any() or bias_zero)
+                out[w, t, h] = int(v.any()) | (int(fast) << 1) | (int(fast and e.all()) << 2)
+    return out
+
+
+def test_tile_class_export_matches_visibility():
+    """The FP8 attention kernel's half-tile classes (the decision that skips the
+    per-score mask), exported through rc_debug_tile_classes and computed with
+    the kernel's own summary and rules, against the visibility definition:
+    exact under the block-causal mask; under the same-block mask "may be
+    visible" is a superset and "fast" exact."""
+    banner("FP8 tile classes vs visibility (wrap, partial tiles, empty slots, multi-block waves)")
+    rng = np.random.default_rng(11)
+    cases = 0
+    # ring A: 300 slots, written from slot 290 (wraps), blocks 0, 2, 4, empty slots left
+    g, o = make_pair(300, 1, 64, "bf16", 0.0, first_slot=290)
+    for b, n in enumerate([40, 70, 33]):
+        write_both(g, o, rng, n, 10 * b, b * 2)
+        g.advance(n)
+        o.advance(n)
+    # ring B: 1,000 FP8 slots, chunks of 96 in blocks 0..11 (wraps, the oldest evicted)
+    gb, ob = make_pair(1000, 2, 128, "fp8", 10000.0, first_slot=700)
+    for b in range(12):
+        write_both(gb, ob, rng, 96, 96 * b, b)
+        gb.advance(96)
+        ob.advance(96)
+    for ring_g, ring_o in ((g, o), (gb, ob)):
+        for n_q, b0, bl in [(1, 0, 1), (90, 0, 20), (300, 1, 7), (64, 4, 64), (17, -3, 5), (96, 11, 96),
+                            (200, 9, 40)]:
+            for bias in (0.0, -0.5):
+                for same in (False, True):
+                    got = ring_g.tile_classes(n_q, b0, bl, bias, same).cpu().numpy()
+                    want = _tile_classes_ref(ring_o.slot_block, n_q, b0, bl, bias, same)
+                    assert got.shape == want.shape
+                    if same:
+                        assert np.array_equal(got & 6, want & 6), (n_q, b0, bl, bias)
+                        assert np.all((got & 1) >= (want & 1)), (n_q, b0, bl, bias)
+                    else:
+                        assert np.array_equal(got, want), (n_q, b0, bl, bias)
+                    cases += 1
+    print(f"  {cases} cases", flush=True)
+
+
 # ------------------------------------------------------------------ long run
 def test_longrun_scaled_schedule():
     """The long-run schedule scaled down: 14 chunks over a 3-chunk ring, a
