@@ -6,10 +6,12 @@
 // (StreamLTX project page, Training).
 //
 // Work split.  A workgroup owns 128 queries of one head and runs 8 waves:
-// 4 query waves of 32 x 2 key halves.  Half k walks the 128-slot tiles
-// k, k + 2, ...; at the end the halves merge their softmax states through
-// LDS.  Tiles move global -> LDS with direct loads, double-buffered, one
-// workgroup barrier per tile.
+// 4 query waves of 32 x 2 key halves.  Half 1 walks the 128-slot tiles
+// 0, 2, ..., half 0 the tiles 1, 3, ...; the two waves of a pair (same
+// queries, different key halves) share the preparation of their queries and,
+// at the end, the merge of their softmax states through LDS (each finishes
+// half of the head dimension).  Tiles move global -> LDS with direct loads,
+// double-buffered, one workgroup barrier per tile.
 //
 // Formulation.  S^T = K Q^T with 16x16x128 FP8 MFMAs: one instruction covers
 // the whole head dimension of 16 slots x 16 queries, and every lane ends up
@@ -30,7 +32,7 @@
 // axis of P V):  P~ = 2^(y + log2 s_v - m) = p s_v,  l += P~ / s_v,  so
 // O = sum P~ Vc needs no rescaling.  Per slot A = c s_k, C = log2(s_v) / A
 // (the accumulator's start value) and 1/s_v are tabulated once per tile.
-// The stabiliser m is raised only when a tile's maximum passes it by
+// The stabiliser m is raised only when a half-tile's maximum passes it by
 // tau = 8 (log2), so P~ <= 256 stays inside e4m3 and O rescales are rare.
 //
 // Precision.  FP8 Q and P carry 3 mantissa bits each; the output error they

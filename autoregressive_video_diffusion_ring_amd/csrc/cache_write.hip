@@ -521,20 +521,20 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
     cc[e] = __shfl(c1, lane * (EPT / 2) + e, kWave);
     ss[e] = __shfl(s1, lane * (EPT / 2) + e, kWave);
   }
-  const int rows = r.H * r.N;
+  // head h = blockIdx.y; slots s0 + i * stride of it (no division per row)
+  const int h = blockIdx.y;
   const int stride = gridDim.x * RPB;
-  for (int row0 = blockIdx.x * RPB + threadIdx.x / LPR; row0 < rows; row0 += kRotRows * stride) {
+  for (int s0 = blockIdx.x * RPB + threadIdx.x / LPR; s0 < r.N; s0 += kRotRows * stride) {
     uint4 raw[kRotRows];
     float sc[kRotRows];
     bool live[kRotRows];
 #pragma unroll
     for (int i = 0; i < kRotRows; ++i) {
-      const int row = row0 + i * stride;
+      const int s = s0 + i * stride;
       live[i] = false;
       raw[i] = make_uint4(0u, 0u, 0u, 0u);
       sc[i] = 0.f;
-      if (row < rows) {
-        const int h = row / r.N, s = row - h * r.N;
+      if (s < r.N) {
         const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
         live[i] = r.slot_block[s] != -1;
         raw[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(r.k) + (srow * D + lane * EPT) * ES);
@@ -543,9 +543,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delt
     }
 #pragma unroll
     for (int i = 0; i < kRotRows; ++i) {
-      const int row = row0 + i * stride;
-      if (row >= rows) continue;  // whole rows (and so whole lane groups) skip together
-      const int h = row / r.N, s = row - h * r.N;
+      const int s = s0 + i * stride;
+      if (s >= r.N) continue;  // whole rows (and so whole lane groups) skip together
       const size_t srow = static_cast<size_t>(h) * r.v_ld + s;
       float x[EPT];
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
@@ -639,9 +638,8 @@ hipError_t rerotate_impl(const RingView& r, int delta, hipStream_t s) {
   RopeTable t = make_rope(r.rope_base, r.d);
   constexpr int LPR = D / (16 / Store<KV>::bytes);
   constexpr int RPB = kThreads / LPR;
-  const int rows = r.H * r.N;
-  const int blocks = std::max(1, std::min((rows + RPB * kRotRows - 1) / (RPB * kRotRows), 4096));
-  hipLaunchKernelGGL((rerotate_kernel<KV, D>), dim3(blocks), dim3(kThreads), 0, s, r, delta, t);
+  const int blocks = std::max(1, std::min((r.N + RPB * kRotRows - 1) / (RPB * kRotRows), 4096));
+  hipLaunchKernelGGL((rerotate_kernel<KV, D>), dim3(blocks, r.H), dim3(kThreads), 0, s, r, delta, t);
   return hipGetLastError();
 }
 
