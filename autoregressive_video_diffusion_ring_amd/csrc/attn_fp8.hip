@@ -892,7 +892,11 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       const float mm = fmaxf(S.m_run[b], m1);
       const float a0 = S.m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run[b] - mm);
       const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-      l_sum[b] = a0 * l_sum[b] + a1 * l1;
+      // the same expression on both halves (key half 0's terms first), so the
+      // two halves of a row are normalised by bit-identical sums
+      const float ah0 = k0 ? a0 : a1, lh0 = k0 ? l_sum[b] : l1;
+      const float ah1 = k0 ? a1 : a0, lh1 = k0 ? l1 : l_sum[b];
+      l_sum[b] = ah0 * lh0 + ah1 * lh1;
 #pragma unroll
       for (int i = 0; i < kHd; ++i) mine[i][b] = a0 * (k0 ? S.o[i][b] : S.o[kHd + i][b]) + a1 * ox[i][b];
       S.m_run[b] = mm;
