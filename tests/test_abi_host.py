@@ -335,3 +335,29 @@ def test_noalloc_attention_rejects_calls_beyond_its_scratch():
     before = state(r)
     assert L.rc_chunk_attention_noalloc(ctypes.byref(r), FAKE, 128, 0, 0, 128, 0.0, 0.0, FAKE, FAKE, None) == RC_ERR_ARG
     assert "no-allocation" in L.rc_last_error().decode() and state(r) == before
+
+
+def test_tile_classes_size_and_rejections():
+    """rc_debug_tile_classes: the size rule, and every argument error refused
+    before a launch (placeholder device pointers, never touched)."""
+    from autoregressive_video_diffusion_ring_amd._lib import RC_MASK_BLOCK_CAUSAL, RC_MASK_SAME_BLOCK
+    L = lib()
+    r = fake_ring(300)
+    for n_q in (1, 32, 33, 757):
+        assert L.rc_debug_tile_classes_bytes(ctypes.byref(r), n_q) == -(-n_q // 32) * -(-300 // 128) * 2
+    assert L.rc_debug_tile_classes_bytes(ctypes.byref(r), 0) == 0
+    need = L.rc_debug_tile_classes_bytes(ctypes.byref(r), 40)
+    before = bytes(r)
+    bad = [
+        (40, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.0, None, need),          # no output buffer
+        (40, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.0, FAKE, need - 1),      # output too small
+        (0, 0, 10, RC_MASK_BLOCK_CAUSAL, 0.0, FAKE, need),           # no queries
+        (40, 0, 0, RC_MASK_BLOCK_CAUSAL, 0.0, FAKE, need),           # zero block length
+        (40, 0, 10, 7, 0.0, FAKE, need),                             # unknown mask
+        (40, 0, 10, RC_MASK_SAME_BLOCK, float("nan"), FAKE, need),   # non-finite bias
+        (40, 0, 10, RC_MASK_BLOCK_CAUSAL, float("inf"), FAKE, need),
+    ]
+    for n_q, b0, bl, mask, bias, out, size in bad:
+        assert L.rc_debug_tile_classes(ctypes.byref(r), n_q, b0, bl, mask, bias, out, size, None) == RC_ERR_ARG, \
+            (n_q, bl, mask, bias, size)
+        assert bytes(r) == before
