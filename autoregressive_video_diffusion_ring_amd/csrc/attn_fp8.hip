@@ -114,7 +114,7 @@ struct Tile {
 
 // Per-slot factors of one tile of one key half (128 entries each, indexed by
 // the slot's place in the tile), then a summary of each half-tile
-// {any slot valid, all valid, min block, max block over valid slots}.  The
+// {any slot occupied, min block, max block over occupied slots, 0}.  The
 // half-tile ht holds the slots 32g + 16ht + 0..15, g = 0..3: the slots whose
 // scores one wave computes between two stabiliser checks.
 constexpr int kFacA = 0, kFacC = kT, kFacIv = 2 * kT, kFacKb = 3 * kT, kFacSum = 4 * kT;
@@ -238,31 +238,33 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 }
 
 // Summary of a half-tile from the block ids of its 64 slots, one per lane
-// (-1 = empty): {any slot valid, all valid, min block, max block over the
-// valid slots}.
+// (-1 = empty): {any slot occupied, min block, max block over the occupied
+// slots, 0}.
 __device__ __forceinline__ v4i half_tile_summary(int kb) {
   const bool kval = kb != -1;
   const uint64_t vb = __ballot(kval);
   const int kmin = wave_minmax_i32<false>(kval ? kb : INT32_MAX);
   const int kmax = wave_minmax_i32<true>(kval ? kb : INT32_MIN);
-  return v4i{vb != 0ull ? 1 : 0, vb == ~0ull ? 1 : 0, kmin, kmax};
+  return v4i{vb != 0ull ? 1 : 0, kmin, kmax, 0};
 }
 
-// Class of a half-tile (summary any, all, kmin, kmax) for a wave whose
-// queries' blocks span qb_lo .. qb_hi.  vis: some slot may be visible to some
-// query (exact under the block-causal mask, a superset under the same-block
-// mask); fast: every slot is visible to every query with one bias value (or
-// the bias is 0), so the per-score mask is skipped; hist: fast with the bias
-// on every score.
+// Class of a half-tile (summary any, kmin, kmax over its occupied slots) for
+// a wave whose queries' blocks span qb_lo .. qb_hi.  vis: some slot may be
+// visible to some query (exact under the block-causal mask, a superset under
+// the same-block mask); fast: every occupied slot is visible to every query
+// with one bias value (or the bias is 0), so the per-score mask is skipped
+// (empty slots need no mask: their factor-table entry starts the QK
+// accumulator at -inf, so their probability is exactly 0); hist: fast with
+// the bias on every score.
 struct HalfTileClass {
   bool vis, fast, hist;
 };
-__device__ __forceinline__ HalfTileClass half_tile_class(int any, int all, int kmin, int kmax, int qb_lo, int qb_hi,
+__device__ __forceinline__ HalfTileClass half_tile_class(int any, int kmin, int kmax, int qb_lo, int qb_hi,
                                                          bool same_block, bool bias_zero) {
-  const bool all_same = qb_lo == qb_hi && all && kmin == qb_lo && kmax == qb_lo;
+  const bool all_same = qb_lo == qb_hi && any && kmin == qb_lo && kmax == qb_lo;
   if (same_block) return {any && kmin <= qb_hi && kmax >= qb_lo, all_same, false};
-  const bool all_vis = all && kmax <= qb_lo;
-  const bool all_hist = all && kmax < qb_lo;
+  const bool all_vis = any && kmax <= qb_lo;
+  const bool all_hist = any && kmax < qb_lo;
   const bool fast = all_vis && (all_hist || all_same || bias_zero);
   return {any && kmin <= qb_hi, fast, fast && all_hist};
 }
@@ -404,7 +406,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
       const float vsc = fmaxf(vs, kMinVScale);
       const float A = fmaxf(c_mul * ks, kMinA);
       tbl[kFacA + fslot] = A;
-      tbl[kFacC + fslot] = __builtin_amdgcn_logf(vsc) * __builtin_amdgcn_rcpf(A);
+      // an empty slot starts its QK accumulator at -inf: every path then
+      // gives it probability 0 without a per-score mask
+      tbl[kFacC + fslot] = kb == -1 ? -INFINITY : __builtin_amdgcn_logf(vsc) * __builtin_amdgcn_rcpf(A);
       tbl[kFacIv + fslot] = __builtin_amdgcn_rcpf(vsc);
       reinterpret_cast<int32_t*>(tbl)[kFacKb + fslot] = kb;
       return;
@@ -590,10 +594,9 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(F8Args a) {
   // tables at kFacSum + 4 ht).
   auto classify = [&](const v4i sm, bool& vis, bool& fast, bool& hist) __attribute__((always_inline)) {
     const int any = __builtin_amdgcn_readfirstlane(sm.x);
-    const int all = __builtin_amdgcn_readfirstlane(sm.y);
-    const int kmin = __builtin_amdgcn_readfirstlane(sm.z);
-    const int kmax = __builtin_amdgcn_readfirstlane(sm.w);
-    const HalfTileClass c = half_tile_class(any, all, kmin, kmax, qb_lo, qb_hi, same_block, a.bias_log2 == 0.f);
+    const int kmin = __builtin_amdgcn_readfirstlane(sm.y);
+    const int kmax = __builtin_amdgcn_readfirstlane(sm.z);
+    const HalfTileClass c = half_tile_class(any, kmin, kmax, qb_lo, qb_hi, same_block, a.bias_log2 == 0.f);
     vis = c.vis;
     fast = c.fast;
     hist = c.hist;
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__(kWave) void tile_class_kernel(const int32_t* slot_b
   if (q < n_q) lo = hi = q_block0 + q / q_block_len;
   lo = wave_minmax_i32<false>(lo);
   hi = wave_minmax_i32<true>(hi);
-  const HalfTileClass c = half_tile_class(sm.x, sm.y, sm.z, sm.w, lo, hi, same_block != 0, bias_zero != 0);
+  const HalfTileClass c = half_tile_class(sm.x, sm.y, sm.z, lo, hi, same_block != 0, bias_zero != 0);
   if (lane == 0) out[item] = static_cast<uint8_t>((c.vis ? 1 : 0) | (c.fast ? 2 : 0) | (c.hist ? 4 : 0));
 }
 

@@ -411,8 +411,10 @@ rc_status rc_debug_visibility(const rc_ring* ring, int32_t n_q, int32_t q_block0
  * 128 t + 32 g + 16 h + 0..15, g = 0..3) the bits
  *   1  vis:  some slot may be visible to some query of the wave (exact under
  *            the block-causal mask; a superset under the same-block mask);
- *   2  fast: every slot is visible to every query of the wave with one bias
- *            value (or cache_bias is 0): the per-score mask is skipped;
+ *   2  fast: the half-tile has an occupied slot, and every occupied slot is
+ *            visible to every query of the wave with one bias value (or
+ *            cache_bias is 0): the per-score mask is skipped (empty slots get
+ *            probability 0 without it);
  *   4  hist: fast, with the bias on every score.
  * classes_bytes >= rc_debug_tile_classes_bytes(ring, n_q), else RC_ERR_ARG;
  * RC_ERR_ARG also for a bad mask, a non-finite bias, n_q or q_block_len < 1.

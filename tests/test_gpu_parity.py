@@ -718,8 +718,10 @@ def test_visibility_export_bit_exact():
 def _tile_classes_ref(slot_block, n_q, q_block0, q_block_len, cache_bias, same):
     """Half-tile classes from the visibility definition: for each 32-query wave,
     128-slot tile and half-tile (slots 32 g + 16 h + 0..15 of the tile), bit 1
-    if some pair is visible, 2 if every pair is visible with one bias value
-    (or the bias is 0), 4 if that value is the bias on every pair."""
+    if some pair is visible, 2 if the half-tile has an occupied slot and every
+    pair with an occupied slot is visible with one bias value (or the bias is
+    0), 4 if that value is the bias on every such pair.  Empty slots need no
+    mask: the kernel gives them probability 0 through its factor table."""
     N = len(slot_block)
     n_t, n_w = -(-N // 128), -(-n_q // 32)
     sb = np.full(n_t * 128, -1, dtype=np.int64)
@@ -732,8 +734,9 @@ def _tile_classes_ref(slot_block, n_q, q_block0, q_block_len, cache_bias, same):
         for t in range(n_t):
             for h in range(2):
                 cols = [128 * t + 32 * g + 16 * h + i for g in range(4) for i in range(16)]
-                v, e = vis[qs][:, cols], earlier[qs][:, cols]
-                fast = bool(v.all()) and (bool(e.all()) or not e.any() or bias_zero)
+                occ = [c for c in cols if sb[c] != -1]
+                v, e = vis[qs][:, occ], earlier[qs][:, occ]
+                fast = bool(occ) and bool(v.all()) and (bool(e.all()) or not e.any() or bias_zero)
                 out[w, t, h] = int(v.any()) | (int(fast) << 1) | (int(fast and e.all()) << 2)
     return out
 
