@@ -18,7 +18,9 @@
 //  * key_mass_kernel: a workgroup of 16 waves owns 512 slots of one head
 //    (32 per wave, K operand and factors in registers) and streams the
 //    head's prepared queries through LDS, 8 tiles of 32 queries at a time,
-//    double-buffered; per tile 2 MFMAs, then exp2(A s + b) summed in the lane.
+//    double-buffered with direct buffer-to-LDS loads (no staging registers,
+//    so two workgroups fit on a compute unit: 8 waves per SIMD); per tile 2
+//    MFMAs, then exp2(A s + b) summed in the lane.
 // Each mass entry is summed by one lane pair in a fixed order (no atomics).
 //
 // Memory choice implements the greedy rule of the C ABI in closed form.
@@ -58,6 +60,20 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at `base` (raw; loads past the end
+// return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from the buffer at lane offset off + uniform offset soff
+// straight into LDS: the wave's 64 lanes fill the 1,024 bytes at lds_wave_base.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_wave_base), 16, static_cast<int>(off),
+                                           static_cast<int>(soff), 0, 0);
+}
 
 // One prepared tile of 32 queries of one head:
 //   [0, 16)    c_mul (float bits), block of the first and of the last query
@@ -156,11 +172,11 @@ __global__ __launch_bounds__(256) void mass_prep_kernel(MassArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
+__global__ __launch_bounds__(kMassThreads, 8) void key_mass_kernel(MassArgs a) {
   using R = Rec<D>;
   constexpr int KS = D / 64;                               // MFMAs per tile
-  constexpr int kBufBytes = kChunkTiles * R::bytes;
-  constexpr int kLoads = (kBufBytes + kMassThreads * 16 - 1) / (kMassThreads * 16);
+  constexpr int kChunkBytes = kChunkTiles * R::bytes;      // prepared bytes per chunk
+  constexpr int kBufBytes = (kChunkBytes + 1023) / 1024 * 1024;  // whole 1 KiB wave loads
   __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufBytes];
 
@@ -189,30 +205,22 @@ __global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
   const float ksc = a.k_scale[static_cast<size_t>(h) * a.v_ld + slot];
   const int kb = a.slot_block[slot];
 
-  // prepared tiles of this head, in chunks of kChunkTiles through LDS
+  // prepared tiles of this head, in chunks of kChunkTiles through LDS: the
+  // chunk's bytes in 1 KiB pieces, piece p loaded by wave p % 16 (a piece
+  // that runs past the head's tiles reads zeros; bytes past the chunk land
+  // in the buffer's unused tail or belong to tiles the loop does not visit)
   const uint8_t* src = a.ws + static_cast<size_t>(h) * a.QT * R::bytes;
+  const __amdgpu_buffer_rsrc_t src_rsrc = make_rsrc(src, static_cast<uint32_t>(a.QT) * R::bytes);
   const int n_chunks = (a.QT + kChunkTiles - 1) / kChunkTiles;
   auto chunk_bytes = [&](int c) { return min(kChunkTiles, a.QT - c * kChunkTiles) * R::bytes; };
-  v4u stage[kLoads];
-  auto fetch = [&](int c) {
+  auto issue = [&](uint8_t* dst, int c) __attribute__((always_inline)) {
     const int nb = chunk_bytes(c);
-    const uint8_t* p = src + static_cast<size_t>(c) * kBufBytes;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int off = (i * kMassThreads + tid) * 16;
-      if (off < nb) stage[i] = *reinterpret_cast<const v4u*>(p + off);
-    }
+    for (int p = wave; p * 1024 < nb; p += kMassWaves)
+      dma16(src_rsrc, static_cast<uint32_t>(lane * 16), static_cast<uint32_t>(c * kChunkBytes + p * 1024),
+            dst + p * 1024);
   };
-  auto put = [&](uint8_t* dst, int c) {
-    const int nb = chunk_bytes(c);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int off = (i * kMassThreads + tid) * 16;
-      if (off < nb) *reinterpret_cast<v4u*>(dst + off) = stage[i];
-    }
-  };
-  fetch(0);
-  put(buf0, 0);
+  issue(buf0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces are in LDS
   __syncthreads();
 
   float acc = 0.f;
@@ -265,16 +273,20 @@ __global__ __launch_bounds__(kMassThreads) void key_mass_kernel(MassArgs a) {
     }
   };
 
-  for (int c = 0; c < n_chunks; ++c) {
-    uint8_t* cur = (c & 1) ? buf1 : buf0;
-    uint8_t* nxt = (c & 1) ? buf0 : buf1;
-    const bool more = c + 1 < n_chunks;
-    if (more) fetch(c + 1);
+  // one chunk from cur while the next one loads into nxt; the two buffers
+  // alternate by call site, so that each LDS read waits only for the loads
+  // into its own buffer
+  auto chunk = [&](const uint8_t* cur, uint8_t* nxt, int c) __attribute__((always_inline)) {
+    if (c + 1 < n_chunks) issue(nxt, c + 1);
     const int tiles = min(kChunkTiles, a.QT - c * kChunkTiles);
     if (active)
       for (int t = 0; t < tiles; ++t) tile(cur + t * R::bytes);
-    if (more) put(nxt, c + 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // chunk c + 1 is in nxt; every wave is done with cur
+  };
+  for (int c = 0; c < n_chunks; c += 2) {
+    chunk(buf0, buf1, c);
+    if (c + 1 < n_chunks) chunk(buf1, buf0, c + 1);
   }
   // lanes n and n + 32 hold the same slot (different queries)
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
