@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kWThreadsFp8) void cache_write_fp8_kernel(WriteArgs
 // Delta re-rotation of every occupied row.  A row of K (d elements) is
 // handled by LPR lanes with 16 bytes each; a thread takes kRotRows rows whose
 // loads are all issued before any of the rows' arithmetic.
-constexpr int kRotRows = 4;
+constexpr int kRotRows = 2;
 
 template <int KV, int D>
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(RingView r, int delta, RopeTable rope) {
