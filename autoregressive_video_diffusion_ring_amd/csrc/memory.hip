@@ -12,8 +12,9 @@
 // would cost a 32-lane reduction per slot and tile inside the hot loop; this
 // separate kernel computes S = Q K^T instead, so that every lane holds ONE
 // slot and 16 queries and the sum over queries stays in the lane:
-//  * mass_prep_kernel: one wave per (head, 32 queries) rotates and quantises
-//    the queries to FP8 (one scale per 32 queries) straight into the MFMA
+//  * mass_prep_kernel: two waves per (head, 32 queries), one per half of the
+//    head dimension, rotate and quantise the queries to FP8 (one scale per
+//    32 queries, their absmax shared through LDS) straight into the MFMA
 //    operand order, with each query's -lse log2(e) and block id;
 //  * key_mass_kernel: a workgroup of 16 waves owns 512 slots of one head
 //    (32 per wave, K operand and factors in registers) and streams the
@@ -111,54 +112,69 @@ struct MassArgs {
 
 template <int D>
 __global__ __launch_bounds__(256) void mass_prep_kernel(MassArgs a) {
+  // two waves per prepared tile: wave half w rotates and quantises the head
+  // dimension's half d = 64 w .. 64 w + 63 (the pieces 2 w, 2 w + 1 of the
+  // operand); the tile's absmax is shared through LDS
   using R = Rec<D>;
+  constexpr int KS = D / 64;
+  static_assert(KS <= 2, "one or two halves of the head dimension");
+  __shared__ float amax_sh[2][2];
   const int lane = threadIdx.x % kWave;
-  const int item = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (item >= a.H * a.QT) return;  // whole waves; no workgroup barrier below
-  const int h = item / a.QT, t = item % a.QT;
+  const int local = threadIdx.x / (2 * kWave);      // tile of this workgroup (0, 1)
+  const int w = (threadIdx.x / kWave) % 2;          // half of the head dimension
+  const int item = blockIdx.x * 2 + local;
+  const bool item_ok = item < a.H * a.QT;            // the workgroup's barrier is reached by every wave
+  const int it = item_ok ? item : 0;
+  const int h = it / a.QT, t = it % a.QT;
   const int n = lane & 31, g = lane >> 5;
   const int qi = t * kMQ + n;
-  const bool q_ok = qi < a.n_q;
-  constexpr int NE = D / 2;  // values of this lane: d = 64 ks + 32 g + e, e < 32
+  const bool q_ok = item_ok && qi < a.n_q;
+  const bool live = w < KS;                         // d 64: one half only
+  constexpr int NE = 32;  // values of this lane: d = 64 w + 32 g + e, e < 32
   float x[NE];
   const uint16_t* qrow = a.q + (static_cast<size_t>(q_ok ? qi : 0) * a.H + h) * D;
   v4u raw[NE / 8];
 #pragma unroll
   for (int r = 0; r < NE / 8; ++r)
-    raw[r] = *reinterpret_cast<const v4u*>(qrow + (r / 4) * 64 + 32 * g + (r % 4) * 8);
+    raw[r] = live ? *reinterpret_cast<const v4u*>(qrow + 64 * w + 32 * g + r * 8) : v4u{0u, 0u, 0u, 0u};
   const long long qpos = static_cast<long long>(a.q_pos0) + qi;
 #pragma unroll
   for (int e = 0; e < NE; e += 2) {
-    const uint32_t w = raw[e / 8][(e / 2) % 4];
-    const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
+    const uint32_t wd = raw[e / 8][(e / 2) % 4];
+    const float x0 = __uint_as_float(wd << 16), x1 = __uint_as_float(wd & 0xFFFF0000u);
     float y0 = x0, y1 = x1;
     if (a.use_rope) {
-      const int j = ((e / 32) * 64 + 32 * g + (e % 32)) >> 1;  // RoPE pair of (d, d + 1)
+      const int j = (64 * w + 32 * g + e) >> 1;  // RoPE pair of (d, d + 1)
       float c, sn;
-      rope_cs_hw(a.rope.rev[j], qpos, &c, &sn);
+      rope_cs_hw(a.rope.rev[live ? j : 0], qpos, &c, &sn);
       y0 = x0 * c - x1 * sn;
       y1 = x0 * sn + x1 * c;
     }
-    x[e] = q_ok ? y0 : 0.f;
-    x[e + 1] = q_ok ? y1 : 0.f;
+    x[e] = q_ok && live ? y0 : 0.f;
+    x[e + 1] = q_ok && live ? y1 : 0.f;
   }
   float am = 0.f;
 #pragma unroll
   for (int e = 0; e < NE; ++e) am = fmaxf(am, fabsf(x[e]));
   am = group_max<kWave>(am);
+  if (lane == 0) amax_sh[local][w] = am;
+  __syncthreads();
+  am = fmaxf(amax_sh[local][0], amax_sh[local][1]);
+  if (!item_ok || !live) return;
   const float sq = am > 0.f ? am / 448.f : 1.f;
   const float iq = am > 0.f ? 448.f / am : 0.f;
   uint8_t* rec = a.ws + static_cast<size_t>(item) * R::bytes;
 #pragma unroll
-  for (int pc = 0; pc < NE / 16; ++pc) {
-    v4u w;
+  for (int part = 0; part < 2; ++part) {
+    v4u wv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int e = 16 * pc + 4 * k;
-      w[k] = cvt_fp8x4(x[e] * iq, x[e + 1] * iq, x[e + 2] * iq, x[e + 3] * iq);
+      const int e = 16 * part + 4 * k;
+      wv[k] = cvt_fp8x4(x[e] * iq, x[e + 1] * iq, x[e + 2] * iq, x[e + 3] * iq);
     }
-    *reinterpret_cast<v4u*>(rec + R::frag + pc * 1024 + lane * 16) = w;
+    *reinterpret_cast<v4u*>(rec + R::frag + (2 * w + part) * 1024 + lane * 16) = wv;
   }
+  if (w != 0) return;
   const int last = min(t * kMQ + kMQ, a.n_q) - 1;
   const int qb_lo = a.q_block0 + (t * kMQ) / a.q_block_len;
   const int qb_hi = a.q_block0 + last / a.q_block_len;
@@ -579,7 +595,7 @@ hipError_t mass_impl(const RingView& r, const AttnCall& c, const float* lse, flo
   for (int j = 0; j < D / 2; ++j)
     a.rope.rev[j] = a.use_rope ? std::pow(static_cast<double>(r.rope_base), -2.0 * j / D) / (2.0 * M_PI) : 0.0;
   const int preps = r.H * a.QT;
-  hipLaunchKernelGGL((mass_prep_kernel<D>), dim3((preps + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((mass_prep_kernel<D>), dim3((preps + 1) / 2), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int groups = (r.v_ld + kMassSlots - 1) / kMassSlots;
